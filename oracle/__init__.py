@@ -1,0 +1,206 @@
+"""CPU oracle for the BitNet b1.58 BitLinear forward pass (W1.58A8).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, `__graft_entry__.smoke()` and the
+CPU-baseline leg of `bench.py` may import this package. The HIP library does not
+depend on it and shares no code with it.
+
+The arithmetic lives in `bitlinear_oracle.c` (plain C loops, one function per
+step of the method); this module marshals numpy arrays and composes the steps in
+the order the pages give:
+
+  pack:     gamma = mean|W|  ->  W~ = RoundClip(W / gamma, -1, 1)  ->  2-bit codes
+  forward:  per-token absmax int8 quantization of x  ->  int32 product with W~
+            ->  y = acc * (s / 127) * gamma
+  ffn:      one quantization of x shared by gate and up  ->  h = relu(g)^2 * u
+            ->  per-token requantization of h  ->  down projection
+
+Sources: "BitNet 1-bit LLM 的混合精度微调技术：渐进量化策略" (BitLinear paragraph,
+operational-parameter paragraph); "BitNet 中使用直通估计器工程化三元权重训练"
+(section 工程化训练流程与参数配置, activation item); "穿越1比特的奇幻旅程" summary of
+the BitNet b1.58 2B4T report (sections 架构创新 and 推理实现 / GPU端).
+
+Parity pins for every function live in tests/test_oracle_pins.py; none of them
+is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_absmean.restype = ctypes.c_float
+    lib.oracle_absmean.argtypes = [_p, _i64, _i64]
+    lib.oracle_ternarize.argtypes = [_p, _i64, _i64, ctypes.c_float, _p]
+    lib.oracle_pack.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_unpack.restype = _i64
+    lib.oracle_unpack.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_quant_act.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_bf16_to_f32.argtypes = [_p, _i64, _p]
+    lib.oracle_matmul_i32.argtypes = [_p, _i64, _i64, _p, _i64, _p]
+    lib.oracle_rescale.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _p]
+    lib.oracle_sqrelu_gate.argtypes = [_p, _p, _i64, _p]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(t: int) -> None:
+    _load().oracle_set_num_threads(int(t))
+
+
+# ------------------------------------------------------------------ steps
+
+def bf16_to_f32(xb: np.ndarray) -> np.ndarray:
+    xb = _c(xb, np.uint16)
+    out = np.empty(xb.shape, dtype=np.float32)
+    _load().oracle_bf16_to_f32(_ptr(xb), xb.size, _ptr(out))
+    return out
+
+
+def absmean(w: np.ndarray) -> np.float32:
+    w = _c(w, np.float32)
+    n, k = w.shape
+    return np.float32(_load().oracle_absmean(_ptr(w), n, k))
+
+
+def ternarize(w: np.ndarray, gamma) -> np.ndarray:
+    w = _c(w, np.float32)
+    n, k = w.shape
+    out = np.empty((n, k), dtype=np.int8)
+    _load().oracle_ternarize(_ptr(w), n, k, float(np.float32(gamma)), _ptr(out))
+    return out
+
+
+def pack(wt: np.ndarray) -> np.ndarray:
+    wt = _c(wt, np.int8)
+    n, k = wt.shape
+    if k % 4:
+        raise ValueError("k must be a multiple of 4")
+    out = np.empty((n, k // 4), dtype=np.uint8)
+    _load().oracle_pack(_ptr(wt), n, k, _ptr(out))
+    return out
+
+
+def unpack(packed: np.ndarray, k: int) -> np.ndarray:
+    """Ternary weights from packed bytes; raises on the invalid code 3."""
+    packed = _c(packed, np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] * 4 != k:
+        raise ValueError("packed width does not match k")
+    out = np.empty((n, k), dtype=np.int8)
+    bad = _load().oracle_unpack(_ptr(packed), n, k, _ptr(out))
+    if bad:
+        raise ValueError(f"{bad} invalid 2-bit codes (3) in packed weights")
+    return out
+
+
+def pack_weights(w: np.ndarray):
+    """Offline weight step: (packed uint8 [n][k/4], gamma fp32, ternary int8 [n][k])."""
+    g = absmean(w)
+    wt = ternarize(w, g)
+    return pack(wt), g, wt
+
+
+def _as_f32_acts(x, dtype: str):
+    if dtype == "bf16":
+        return bf16_to_f32(x)
+    if dtype == "f32":
+        return _c(x, np.float32)
+    raise ValueError(dtype)
+
+
+def quant_act(x: np.ndarray, dtype: str = "f32"):
+    """(q int8 [m][k], s fp32 [m]) for activations x (fp32, or bf16 bit patterns)."""
+    xf = _as_f32_acts(x, dtype)
+    m, k = xf.shape
+    q = np.empty((m, k), dtype=np.int8)
+    s = np.empty(m, dtype=np.float32)
+    _load().oracle_quant_act(_ptr(xf), m, k, _ptr(q), _ptr(s))
+    return q, s
+
+
+def matmul_i32(q: np.ndarray, wt: np.ndarray) -> np.ndarray:
+    q = _c(q, np.int8)
+    wt = _c(wt, np.int8)
+    m, k = q.shape
+    n, k2 = wt.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    acc = np.empty((m, n), dtype=np.int32)
+    _load().oracle_matmul_i32(_ptr(q), m, k, _ptr(wt), n, _ptr(acc))
+    return acc
+
+
+def rescale(acc: np.ndarray, s: np.ndarray, gamma) -> np.ndarray:
+    acc = _c(acc, np.int32)
+    s = _c(s, np.float32)
+    m, n = acc.shape
+    y = np.empty((m, n), dtype=np.float32)
+    _load().oracle_rescale(_ptr(acc), m, n, _ptr(s), float(np.float32(gamma)), _ptr(y))
+    return y
+
+
+def sqrelu_gate(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    h = np.empty(g.shape, dtype=np.float32)
+    _load().oracle_sqrelu_gate(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+# ------------------------------------------------------------ compositions
+
+def forward(x: np.ndarray, packed: np.ndarray, gamma, k: int, dtype: str = "f32"):
+    """BitLinear forward from packed weights. Returns dict(q, s, acc, y)."""
+    wt = unpack(packed, k)
+    q, s = quant_act(x, dtype)
+    acc = matmul_i32(q, wt)
+    y = rescale(acc, s, gamma)
+    return dict(q=q, s=s, acc=acc, y=y)
+
+
+def ffn(x: np.ndarray, gate, up, down, hidden: int, ffn_dim: int, dtype: str = "bf16"):
+    """Squared-ReLU gated FFN of BitLinear layers. gate/up/down are (packed, gamma)
+    pairs with packed shapes [ffn][hidden/4], [ffn][hidden/4], [hidden][ffn/4].
+    Returns dict(q, s, g, u, h, qh, sh, acc_down, y)."""
+    wg = unpack(gate[0], hidden)
+    wu = unpack(up[0], hidden)
+    wd = unpack(down[0], ffn_dim)
+    q, s = quant_act(x, dtype)
+    g = rescale(matmul_i32(q, wg), s, gate[1])
+    u = rescale(matmul_i32(q, wu), s, up[1])
+    h = sqrelu_gate(g, u)
+    qh, sh = quant_act(h, "f32")
+    acc_d = matmul_i32(qh, wd)
+    y = rescale(acc_d, sh, down[1])
+    return dict(q=q, s=s, g=g, u=u, h=h, qh=qh, sh=sh, acc_down=acc_d, y=y)
