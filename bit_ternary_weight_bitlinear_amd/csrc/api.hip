@@ -1,0 +1,300 @@
+// api.hip -- the extern "C" boundary of the gfx950 BitLinear library.
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued, lays out the caller's workspace, and enqueues kernels on the
+// caller's stream. Nothing here allocates, synchronises or keeps state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace bl;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kRowPad = 256;  // activation rows are padded to the largest GEMM row tile
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void *p) { return aligned(p, 16); }
+
+bool dim_ok(int64_t d) { return d >= 1 && d <= BL_MAX_DIM; }
+bool kdim_ok(int64_t k) { return k >= 4 && k <= BL_MAX_DIM && k % 4 == 0; }
+bool tokens_ok(int64_t m) { return m >= 1 && m <= BL_MAX_TOKENS; }
+
+// bump allocator over the caller's workspace
+struct Carve {
+    char *base;
+    int64_t off = 0;
+    explicit Carve(void *b) : base(static_cast<char *>(b)) {}
+    template <typename T>
+    T *take(int64_t bytes)
+    {
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += round_up(bytes, kAlign);
+        return p;
+    }
+};
+
+// ---- layouts (shared by the size query and the calls)
+struct FwdLayout {
+    bool gemv;
+    int64_t kp;
+    int8_t *qp = nullptr;
+    float *s = nullptr;
+    int32_t *sumq = nullptr;
+    uint8_t *wpad = nullptr;
+    int64_t bytes = 0;
+};
+
+FwdLayout forward_layout(void *ws, int64_t m, int64_t k, int64_t n, bool force_gemm)
+{
+    FwdLayout L;
+    L.kp = round_up(k, 64);
+    L.gemv = !force_gemm && gemv_supported(m, L.kp);
+    Carve c(ws);
+    if (!L.gemv) {
+        const int64_t mp = round_up(m, kRowPad);
+        L.qp = c.take<int8_t>(mp * L.kp);
+        L.s = c.take<float>(mp * 4);
+        L.sumq = c.take<int32_t>(mp * 4);
+    }
+    if (k % 64) L.wpad = c.take<uint8_t>(n * (L.kp / 4));
+    L.bytes = c.off;
+    return L;
+}
+
+struct FfnLayout {
+    bool gemv;
+    int64_t hp, fp;
+    int8_t *qx = nullptr, *qh = nullptr;
+    float *sx = nullptr, *sh = nullptr, *h = nullptr;
+    int32_t *sumx = nullptr, *sumh = nullptr;
+    uint8_t *gpad = nullptr, *upad = nullptr, *dpad = nullptr;
+    int64_t bytes = 0;
+};
+
+FfnLayout ffn_layout(void *ws, int64_t m, int64_t hidden, int64_t ffn)
+{
+    FfnLayout L;
+    L.hp = round_up(hidden, 64);
+    L.fp = round_up(ffn, 64);
+    L.gemv = gemv_supported(m, L.hp) && gemv_supported(m, L.fp);
+    Carve c(ws);
+    L.h = c.take<float>(m * ffn * 4);
+    if (!L.gemv) {
+        const int64_t mp = round_up(m, kRowPad);
+        L.qx = c.take<int8_t>(mp * L.hp);
+        L.sx = c.take<float>(mp * 4);
+        L.sumx = c.take<int32_t>(mp * 4);
+        L.qh = c.take<int8_t>(mp * L.fp);
+        L.sh = c.take<float>(mp * 4);
+        L.sumh = c.take<int32_t>(mp * 4);
+    }
+    if (hidden % 64) {
+        L.gpad = c.take<uint8_t>(ffn * (L.hp / 4));
+        L.upad = c.take<uint8_t>(ffn * (L.hp / 4));
+    }
+    if (ffn % 64) L.dpad = c.take<uint8_t>(hidden * (L.fp / 4));
+    L.bytes = c.off;
+    return L;
+}
+
+bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+bl_status check_ws(void *ws, size_t ws_bytes, int64_t need)
+{
+    if (need == 0) return BL_OK;
+    if (!ws) return BL_ERR_NULL;
+    if (!aligned(ws, kAlign)) return BL_ERR_ALIGN;
+    if ((int64_t)ws_bytes < need) return BL_ERR_WORKSPACE;
+    return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n)
+{
+    switch (op) {
+    case BL_OP_PACK:
+        if (!dim_ok(n) || !kdim_ok(k)) return 0;
+        return (size_t)round_up(n * 8, kAlign);
+    case BL_OP_FORWARD:
+        if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return 0;
+        return (size_t)forward_layout(nullptr, m, k, n, false).bytes;
+    case BL_OP_GEMM_I32:
+        if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return 0;
+        return (size_t)forward_layout(nullptr, m, k, n, true).bytes;
+    case BL_OP_FFN:
+        if (!tokens_ok(m) || !kdim_ok(k) || !kdim_ok(n)) return 0;
+        return (size_t)ffn_layout(nullptr, m, k, n).bytes;
+    default:
+        return 0;
+    }
+}
+
+const char *bitlinear_status_string(int status)
+{
+    switch (status) {
+    case BL_OK: return "BL_OK";
+    case BL_ERR_NULL: return "BL_ERR_NULL: a required pointer is NULL";
+    case BL_ERR_SHAPE: return "BL_ERR_SHAPE: invalid shape (m, n >= 1; k >= 4, k % 4 == 0; within limits)";
+    case BL_ERR_ALIGN: return "BL_ERR_ALIGN: a device pointer is not suitably aligned";
+    case BL_ERR_DTYPE: return "BL_ERR_DTYPE: unknown activation dtype";
+    case BL_ERR_WORKSPACE: return "BL_ERR_WORKSPACE: workspace smaller than bitlinear_workspace_size()";
+    case BL_ERR_HIP: return "BL_ERR_HIP: a kernel launch failed";
+    default: return "unknown bitlinear status";
+    }
+}
+
+bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k, uint8_t *packed, float *gamma,
+                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!w || !packed || !gamma) return BL_ERR_NULL;
+    if (!dim_ok(n) || !kdim_ok(k)) return BL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(packed) || !aligned(gamma, 4)) return BL_ERR_ALIGN;
+    const bl_status ws = check_ws(workspace, workspace_bytes, round_up(n * 8, kAlign));
+    if (ws != BL_OK) return ws;
+    return hip_status(launch_pack(w, n, k, packed, gamma, static_cast<double *>(workspace),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *q, float *scale,
+                              void *stream)
+{
+    if (!x || !q || !scale) return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!tokens_ok(m) || !kdim_ok(k)) return BL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned(scale, 4)) return BL_ERR_ALIGN;
+    return hip_status(launch_act_quant(x, dtype == BL_BF16, m, k, round_up(k, 64), q, nullptr, scale,
+                                       nullptr, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k, const uint8_t *packed,
+                            const float *gamma, int64_t n, float *y, int32_t *acc_out, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    if (!x || !packed || !gamma || !y) return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return BL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned(gamma, 4) ||
+        (acc_out && !aligned16(acc_out)))
+        return BL_ERR_ALIGN;
+    const FwdLayout need = forward_layout(nullptr, m, k, n, false);
+    const bl_status wss = check_ws(workspace, workspace_bytes, need.bytes);
+    if (wss != BL_OK) return wss;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdLayout L = forward_layout(workspace, m, k, n, false);
+    const uint8_t *w = packed;
+    if (L.wpad) {
+        if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
+        w = L.wpad;
+    }
+    if (L.gemv) {
+        GemvProblem p{};
+        p.x = x; p.bf16 = dtype == BL_BF16; p.m = m; p.k = k; p.kp = L.kp; p.n = n;
+        p.w0 = w; p.w1 = nullptr; p.ldw = L.kp / 4; p.gamma0 = gamma; p.gamma1 = nullptr;
+        p.out = y; p.acc_out = acc_out;
+        return hip_status(launch_gemv(p, st));
+    }
+    if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, k, L.kp, nullptr, L.qp, L.s, L.sumq, st))
+        return hip_status(e);
+    GemmProblem g{};
+    g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
+    g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
+    g.out = y; g.acc_out = acc_out; g.epi = EPI_Y;
+    return hip_status(launch_gemm(g, st));
+}
+
+bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
+                             int32_t *acc, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !packed || !acc) return BL_ERR_NULL;
+    if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return BL_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(packed) || !aligned16(acc)) return BL_ERR_ALIGN;
+    const FwdLayout need = forward_layout(nullptr, m, k, n, true);
+    const bl_status wss = check_ws(workspace, workspace_bytes, need.bytes);
+    if (wss != BL_OK) return wss;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdLayout L = forward_layout(workspace, m, k, n, true);
+    const uint8_t *w = packed;
+    if (L.wpad) {
+        if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
+        w = L.wpad;
+    }
+    if (hipError_t e = launch_perm_q(q, m, k, L.kp, L.qp, L.sumq, st)) return hip_status(e);
+    GemmProblem g{};
+    g.qp = L.qp; g.kp = L.kp; g.s = nullptr; g.sumq = L.sumq; g.m = m; g.n = n;
+    g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = nullptr; g.gamma1 = nullptr;
+    g.out = nullptr; g.acc_out = acc; g.epi = EPI_ACC;
+    return hip_status(launch_gemm(g, st));
+}
+
+bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int64_t ffn,
+                        const uint8_t *gate_packed, const float *gate_gamma, const uint8_t *up_packed,
+                        const float *up_gamma, const uint8_t *down_packed, const float *down_gamma,
+                        float *y, int8_t *hq_out, float *hs_out, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    if (!x || !gate_packed || !gate_gamma || !up_packed || !up_gamma || !down_packed || !down_gamma || !y)
+        return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!tokens_ok(m) || !kdim_ok(hidden) || !kdim_ok(ffn)) return BL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(gate_packed) || !aligned16(up_packed) || !aligned16(down_packed) ||
+        !aligned16(y) || !aligned(gate_gamma, 4) || !aligned(up_gamma, 4) || !aligned(down_gamma, 4) ||
+        (hq_out && !aligned16(hq_out)) || (hs_out && !aligned(hs_out, 4)))
+        return BL_ERR_ALIGN;
+    const FfnLayout need = ffn_layout(nullptr, m, hidden, ffn);
+    const bl_status wss = check_ws(workspace, workspace_bytes, need.bytes);
+    if (wss != BL_OK) return wss;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FfnLayout L = ffn_layout(workspace, m, hidden, ffn);
+    const uint8_t *wg = gate_packed, *wu = up_packed, *wd = down_packed;
+    if (L.gpad) {
+        if (hipError_t e = launch_pad_weights(gate_packed, ffn, hidden, L.hp, L.gpad, st)) return hip_status(e);
+        if (hipError_t e = launch_pad_weights(up_packed, ffn, hidden, L.hp, L.upad, st)) return hip_status(e);
+        wg = L.gpad;
+        wu = L.upad;
+    }
+    if (L.dpad) {
+        if (hipError_t e = launch_pad_weights(down_packed, hidden, ffn, L.fp, L.dpad, st)) return hip_status(e);
+        wd = L.dpad;
+    }
+    if (L.gemv) {
+        GemvProblem p{};
+        p.x = x; p.bf16 = dtype == BL_BF16; p.m = m; p.k = hidden; p.kp = L.hp; p.n = ffn;
+        p.w0 = wg; p.w1 = wu; p.ldw = L.hp / 4; p.gamma0 = gate_gamma; p.gamma1 = up_gamma;
+        p.out = L.h;
+        if (hipError_t e = launch_gemv(p, st)) return hip_status(e);
+        GemvProblem d{};
+        d.x = L.h; d.bf16 = false; d.m = m; d.k = ffn; d.kp = L.fp; d.n = hidden;
+        d.w0 = wd; d.w1 = nullptr; d.ldw = L.fp / 4; d.gamma0 = down_gamma; d.gamma1 = nullptr;
+        d.out = y; d.acc_out = nullptr; d.q_out = hq_out; d.s_out = hs_out;
+        return hip_status(launch_gemv(d, st));
+    }
+    if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, hidden, L.hp, nullptr, L.qx, L.sx, L.sumx, st))
+        return hip_status(e);
+    GemmProblem g{};
+    g.qp = L.qx; g.kp = L.hp; g.s = L.sx; g.sumq = L.sumx; g.m = m; g.n = ffn;
+    g.w0 = wg; g.w1 = wu; g.ldw = L.hp / 4; g.gamma0 = gate_gamma; g.gamma1 = up_gamma;
+    g.out = L.h; g.acc_out = nullptr; g.epi = EPI_GATE;
+    if (hipError_t e = launch_gemm(g, st)) return hip_status(e);
+    float *sh = hs_out ? hs_out : L.sh;  // the requantization scales go straight to hs_out if asked
+    if (hipError_t e = launch_act_quant(L.h, false, m, ffn, L.fp, hq_out, L.qh, sh, L.sumh, st))
+        return hip_status(e);
+    GemmProblem d{};
+    d.qp = L.qh; d.kp = L.fp; d.s = sh; d.sumq = L.sumh; d.m = m; d.n = hidden;
+    d.w0 = wd; d.w1 = nullptr; d.ldw = L.fp / 4; d.gamma0 = down_gamma; d.gamma1 = nullptr;
+    d.out = y; d.acc_out = nullptr; d.epi = EPI_Y;
+    return hip_status(launch_gemm(d, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// common.hpp -- device helpers shared by the gfx950 BitLinear kernels.
+//
+// Internal int8 activation layout ("qperm"): every token row is padded with
+// zeros to kp = roundup(k, 64) bytes, and inside each 16-byte group the 4x4
+// byte block is transposed: byte 4*i + b of group g holds q[16*g + 4*b + i].
+// With that order, dword i of a group lines up byte-for-byte with the i-th
+// 2-bit field of the packed weight dword covering the same 16 inputs
+// ((w >> 2i) & 0x03030303 holds the codes of inputs 16g + 4b + i), so
+// both the v_dot4 decode path and the MFMA operands read the activations
+// with plain 16-byte loads and no per-element shuffles.
+//
+// Codes are kept as w+1 in {0,1,2}; the products then carry an offset that is
+// removed once per token: sum_k q*w = sum_k q*code - sum_k q ("sumq").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: data read once, keep it out of the caches)
+__device__ inline uint4 load_nt16(const void *p)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr int kThreads = 256;
+constexpr float kEps = 1e-5f;
+
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// byte offset, inside a row of the qperm layout, of input index k
+__device__ inline int qperm_index(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+
+// ---------------------------------------------------------------- DPP reductions
+// Butterfly inside each 16-lane row with DPP (quad_perm xor1, quad_perm xor2,
+// row_half_mirror, row_mirror), then across the four rows with lane shuffles.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ inline int dpp_mov(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+
+__device__ inline float wave_max(float v)
+{
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v))));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ inline int wave_sum(int v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    v += dpp_mov<kDppRowHalfMirror>(v);
+    v += dpp_mov<kDppRowMirror>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------- activation loads
+struct bf16_t { uint16_t bits; };
+
+__device__ inline float to_f32(float v) { return v; }
+__device__ inline float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v.bits << 16); }
+
+// Loads the 16 inputs of group g (inputs 16g .. 16g+15) of one row into f[];
+// inputs at or beyond k read as 0. VEC: the row start is 16-byte aligned and
+// k is a multiple of the 16-byte element count, so full groups use 16-byte loads.
+template <typename T, bool VEC>
+__device__ inline void load_group(const T *row, int64_t k, int64_t g, float f[16])
+{
+    const int64_t k0 = g * 16;
+    if (k0 + 16 <= k) {
+        if constexpr (VEC) {
+            if constexpr (sizeof(T) == 4) {
+                const float4 *p = reinterpret_cast<const float4 *>(row + k0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float4 v = p[j];
+                    f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+                }
+            } else {
+                const uint4 *p = reinterpret_cast<const uint4 *>(row + k0);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    uint4 v = p[j];
+                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
+                        f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                    }
+                }
+            }
+        } else {
+            // rows are at least 8-byte aligned (k % 4 == 0): 4 inputs per load
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(T) == 4) {
+                    float4 v = reinterpret_cast<const float4 *>(row + k0)[j];
+                    f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+                } else {
+                    uint2 v = reinterpret_cast<const uint2 *>(row + k0)[j];
+                    f[4 * j + 0] = __uint_as_float(v.x << 16);
+                    f[4 * j + 1] = __uint_as_float(v.x & 0xFFFF0000u);
+                    f[4 * j + 2] = __uint_as_float(v.y << 16);
+                    f[4 * j + 3] = __uint_as_float(v.y & 0xFFFF0000u);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[j] = (k0 + j < k) ? to_f32(row[k0 + j]) : 0.0f;
+    }
+}
+
+// clamp(rint(v * inv), -127, 127) -- the per-token int8 code
+__device__ inline int quant_i8(float v, float inv)
+{
+    float r = __builtin_rintf(v * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Packs the 16 codes of a group into the qperm byte order (4x4 transpose):
+// dword i = bytes (q[i], q[4+i], q[8+i], q[12+i]).
+__device__ inline uint4 qperm_pack(const int q[16])
+{
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d[i] = (uint32_t)(q[i] & 0xFF) | ((uint32_t)(q[4 + i] & 0xFF) << 8) |
+               ((uint32_t)(q[8 + i] & 0xFF) << 16) | ((uint32_t)(q[12 + i] & 0xFF) << 24);
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// Natural byte order of the same 16 codes.
+__device__ inline uint4 qnat_pack(const int q[16])
+{
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d[i] = (uint32_t)(q[4 * i] & 0xFF) | ((uint32_t)(q[4 * i + 1] & 0xFF) << 8) |
+               ((uint32_t)(q[4 * i + 2] & 0xFF) << 16) | ((uint32_t)(q[4 * i + 3] & 0xFF) << 24);
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// Rescale of one accumulator: y = (float)acc * ((s / 127) * gamma)
+__device__ inline float token_scale(float s, float gamma) { return (s / 127.0f) * gamma; }
+
+__device__ inline float sq_relu_gate(float g, float u)
+{
+    float gp = g > 0.0f ? g : 0.0f;
+    return (gp * gp) * u;
+}
+
+}  // namespace bl
