@@ -58,39 +58,44 @@ def cpu_model() -> str:
 # --------------------------------------------------------------------------- helpers
 
 class Timer:
-    """Events on torch's current stream (the stream the library launches on)."""
+    """Times work on torch's current stream (the stream the library launches on)
+    with HIP events. Steps are captured into a HIP graph first, so the host's
+    launch overhead is not part of the measurement; the graph is replayed."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.stream = torch.cuda.current_stream()
 
-    def region(self, fn, steps):
+    def capture(self, fn, n):
         t = self.torch
-        t.cuda.synchronize()
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        for i in range(steps):
-            fn(i)
-        b.record(self.stream)
-        t.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3  # seconds
-
-    def per_launch(self, launches, steps):
-        """launches: list of callables (i) -> None, each one kernel launch of the
-        dominant kernel. Returns the mean event-measured duration per launch (s)."""
-        t = self.torch
-        t.cuda.synchronize()
-        evs = []
-        for i in range(steps):
-            for fn in launches:
-                a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-                a.record(self.stream)
+        g = t.cuda.CUDAGraph()
+        side = t.cuda.Stream()
+        side.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(side):
+            fn(0)  # one eager call on the capture stream before capturing
+        t.cuda.current_stream().wait_stream(side)
+        with t.cuda.graph(g):
+            for i in range(n):
                 fn(i)
-                b.record(self.stream)
-                evs.append((a, b))
         t.cuda.synchronize()
-        d = [a.elapsed_time(b) / 1e3 for a, b in evs]
-        return float(np.mean(d)), float(np.median(d))
+        return g
+
+    def graph_region(self, fn, steps, per_graph):
+        """Replays a graph of `per_graph` steps until >= steps are done.
+        Returns (seconds per step, steps done)."""
+        t = self.torch
+        g = self.capture(fn, per_graph)
+        reps = max(1, -(-steps // per_graph))
+        g.replay()  # warm replay
+        t.cuda.synchronize()
+        st = t.cuda.current_stream()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            g.replay()
+        b.record(st)
+        t.cuda.synchronize()
+        done = reps * per_graph
+        return a.elapsed_time(b) / 1e3 / done, done
 
 
 def make_weights(bl, torch, cfg, tid, n, k, dev):
@@ -135,14 +140,18 @@ def bench_decode(bl, torch, dev, steps, warmup, pool_mb):
     for i in range(warmup):
         step(i)
     tm = Timer(torch)
-    t = tm.region(step, steps)
-    launches = [lambda i, j=j: bl.forward(xs[j], pool[i % len(pool)][j][0], pool[i % len(pool)][j][1],
-                                          out=ys[j]) for j in range(2)]
-    mean_launch, med_launch = tm.per_launch(launches, steps)
-    ms = t / steps * 1e3
-    res = dict(ms_per_step=ms, packed_bytes_per_step=packed_bytes,
-               gbs=packed_bytes / (t / steps) / 1e9,
-               kernel_mean_s=mean_launch, kernel_median_s=med_launch,
+    t_step, done = tm.graph_region(step, steps, len(pool))
+    # the dominant kernel alone, per shape: a graph of launches of one matrix, cycling the pool
+    per_shape = []
+    for j in range(2):
+        def one(i, j=j):
+            ws = pool[i % len(pool)]
+            bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
+        tl, _ = tm.graph_region(one, steps, len(pool))
+        per_shape.append(tl)
+    res = dict(ms_per_step=t_step * 1e3, steps_done=done, packed_bytes_per_step=packed_bytes,
+               gbs=packed_bytes / t_step / 1e9,
+               kernel_mean_s=float(np.mean(per_shape)), kernel_per_shape_s=per_shape,
                algo_bytes_per_launch=float(np.mean(algo_bytes)),
                pool_bytes=pool_bytes, shapes=cfg["mats"])
     return res, (mats, xs)
@@ -164,11 +173,10 @@ def bench_prefill(bl, torch, dev, steps, warmup):
 
     for i in range(warmup):
         step(i)
-    tm = Timer(torch)
-    t = tm.region(step, steps)
+    t, _ = Timer(torch).graph_region(step, steps, min(steps, 8))
     ops = sum(2.0 * m * n * k for k, n in cfg["mats"])
-    return dict(ms_per_step=t / steps * 1e3, tops=ops / (t / steps) / 1e12, ops_per_step=ops,
-                frac_of_mfma_peak=ops / (t / steps) / 1e12 / INT8_MFMA_PEAK_TOPS, m=m, shapes=cfg["mats"])
+    return dict(ms_per_step=t * 1e3, tops=ops / t / 1e12, ops_per_step=ops,
+                frac_of_mfma_peak=ops / t / 1e12 / INT8_MFMA_PEAK_TOPS, m=m, shapes=cfg["mats"])
 
 
 def bench_layer(bl, torch, dev, steps, warmup, pool_mb):
@@ -191,9 +199,9 @@ def bench_layer(bl, torch, dev, steps, warmup, pool_mb):
 
         for i in range(warmup):
             step(i)
-        t = Timer(torch).region(step, steps)
-        out[f"m{m}"] = dict(ms_per_step=t / steps * 1e3, packed_gbs=packed_bytes / (t / steps) / 1e9,
-                            frac_of_hbm_peak=packed_bytes / (t / steps) / 1e9 / HBM_PEAK_GBS)
+        t, _ = Timer(torch).graph_region(step, steps, len(pool))
+        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9,
+                            frac_of_hbm_peak=packed_bytes / t / 1e9 / HBM_PEAK_GBS)
     out["packed_bytes_per_layer"] = packed_bytes
     out["pool_bytes"] = pool_bytes
     return out
@@ -216,10 +224,9 @@ def bench_ffn(bl, torch, dev, steps, warmup):
 
         for i in range(warmup):
             step(i)
-        t = Timer(torch).region(step, steps)
+        t, _ = Timer(torch).graph_region(step, steps, min(steps, 8))
         ops = 2.0 * m * 3 * f * hid
-        out[f"m{m}"] = dict(ms_per_step=t / steps * 1e3, packed_gbs=packed_bytes / (t / steps) / 1e9,
-                            tops=ops / (t / steps) / 1e12)
+        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9, tops=ops / t / 1e12)
     return out
 
 
@@ -292,7 +299,7 @@ def main():
                     kernel="gemv_kernel (decode, fused act-quant + v_dot4)",
                     algo_bytes_per_launch=dec["algo_bytes_per_launch"],
                     mean_launch_us=round(dec["kernel_mean_s"] * 1e6, 3),
-                    median_launch_us=round(dec["kernel_median_s"] * 1e6, 3))
+                    per_shape_launch_us=[round(v * 1e6, 3) for v in dec["kernel_per_shape_s"]])
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -300,7 +307,7 @@ def main():
         "value": round(dec["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": dec["steps_done"],
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 6),
         "higher_is_better": True,

@@ -35,9 +35,8 @@ __device__ inline int block_sum(int v, int *red)
 }
 
 // natural-order store of group g: inputs 16g .. min(16g+16, k) (k % 4 == 0, rows 4-byte aligned)
-__device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const int qi[16])
+__device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const uint4 v)
 {
-    const uint4 v = qnat_pack(qi);
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
     uint32_t *p = reinterpret_cast<uint32_t *>(row + 16 * g);
 #pragma unroll
@@ -49,7 +48,7 @@ __device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const int qi
 
 constexpr int kResidentGroups = 4;
 
-template <typename T, bool VEC>
+template <typename T, bool FULL>
 __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x, int64_t k, int64_t kp,
                                                         int8_t *__restrict__ q_nat,
                                                         int8_t *__restrict__ q_perm,
@@ -69,7 +68,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
         for (int r = 0; r < kResidentGroups; ++r) {
             const int64_t g = threadIdx.x + r * kThreads;
             if (g < G) {
-                load_group<T, VEC>(row, k, g, v[r]);
+                load_group<T, FULL>(row, k, g, v[r]);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[r][j]));
             }
@@ -77,7 +76,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     } else {
         for (int64_t g = threadIdx.x; g < G; g += kThreads) {
             float f[16];
-            load_group<T, VEC>(row, k, g, f);
+            load_group<T, FULL>(row, k, g, f);
 #pragma unroll
             for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(f[j]));
         }
@@ -88,14 +87,10 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
 
     int qsum = 0;
     auto emit = [&](int64_t g, const float f[16]) {
-        int qi[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            qi[j] = quant_i8(f[j], inv);
-            qsum += qi[j];
-        }
-        if (q_perm) *reinterpret_cast<uint4 *>(q_perm + t * kp + 16 * g) = qperm_pack(qi);
-        if (q_nat) store_nat(q_nat + t * k, k, g, qi);
+        uint4 pv, nv;
+        qsum += quant_group(f, inv, &pv, &nv);
+        if (q_perm) *reinterpret_cast<uint4 *>(q_perm + t * kp + 16 * g) = pv;
+        if (q_nat) store_nat(q_nat + t * k, k, g, nv);
     };
     if (resident) {
 #pragma unroll
@@ -106,7 +101,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     } else {
         for (int64_t g = threadIdx.x; g < G; g += kThreads) {
             float f[16];
-            load_group<T, VEC>(row, k, g, f);
+            load_group<T, FULL>(row, k, g, f);
             emit(g, f);
         }
     }
@@ -123,17 +118,23 @@ hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int6
                             int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
 {
     const dim3 grid((unsigned)m), block(kThreads);
+    const bool full = k % 16 == 0;
     if (bf16) {
         const bf16_t *xb = static_cast<const bf16_t *>(x);
-        if (k % 8 == 0)
+        if (full)
             hipLaunchKernelGGL((act_quant_kernel<bf16_t, true>), grid, block, 0, st, xb, k, kp, q_nat,
                                q_perm, s, sumq);
         else
             hipLaunchKernelGGL((act_quant_kernel<bf16_t, false>), grid, block, 0, st, xb, k, kp, q_nat,
                                q_perm, s, sumq);
     } else {
-        hipLaunchKernelGGL((act_quant_kernel<float, true>), grid, block, 0, st,
-                           static_cast<const float *>(x), k, kp, q_nat, q_perm, s, sumq);
+        const float *xf = static_cast<const float *>(x);
+        if (full)
+            hipLaunchKernelGGL((act_quant_kernel<float, true>), grid, block, 0, st, xf, k, kp, q_nat,
+                               q_perm, s, sumq);
+        else
+            hipLaunchKernelGGL((act_quant_kernel<float, false>), grid, block, 0, st, xf, k, kp, q_nat,
+                               q_perm, s, sumq);
     }
     return hipGetLastError();
 }

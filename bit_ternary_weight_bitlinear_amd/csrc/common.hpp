@@ -77,49 +77,48 @@ struct bf16_t { uint16_t bits; };
 __device__ inline float to_f32(float v) { return v; }
 __device__ inline float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v.bits << 16); }
 
-// Loads the 16 inputs of group g (inputs 16g .. 16g+15) of one row into f[];
-// inputs at or beyond k read as 0. VEC: the row start is 16-byte aligned and
-// k is a multiple of the 16-byte element count, so full groups use 16-byte loads.
-template <typename T, bool VEC>
+// Loads the 16 inputs of group g (inputs 16g .. 16g+15) of one row into f[].
+// FULL: k % 16 == 0, so every group is whole and the row start is 16-byte
+// aligned: straight 16-byte loads with no bounds checks (and no branches).
+// Otherwise whole groups use 16-byte (fp32) or 8-byte (bf16) loads -- rows are
+// at least 8-byte aligned since k % 4 == 0 -- and inputs at or beyond k read as 0.
+template <typename T, bool FULL>
 __device__ inline void load_group(const T *row, int64_t k, int64_t g, float f[16])
 {
     const int64_t k0 = g * 16;
-    if (k0 + 16 <= k) {
-        if constexpr (VEC) {
-            if constexpr (sizeof(T) == 4) {
-                const float4 *p = reinterpret_cast<const float4 *>(row + k0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float4 v = p[j];
-                    f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
-                }
-            } else {
-                const uint4 *p = reinterpret_cast<const uint4 *>(row + k0);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    uint4 v = p[j];
-                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
-                        f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-                    }
-                }
-            }
-        } else {
-            // rows are at least 8-byte aligned (k % 4 == 0): 4 inputs per load
+    if constexpr (FULL) {
+        if constexpr (sizeof(T) == 4) {
+            const float4 *p = reinterpret_cast<const float4 *>(row + k0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (sizeof(T) == 4) {
-                    float4 v = reinterpret_cast<const float4 *>(row + k0)[j];
-                    f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
-                } else {
-                    uint2 v = reinterpret_cast<const uint2 *>(row + k0)[j];
-                    f[4 * j + 0] = __uint_as_float(v.x << 16);
-                    f[4 * j + 1] = __uint_as_float(v.x & 0xFFFF0000u);
-                    f[4 * j + 2] = __uint_as_float(v.y << 16);
-                    f[4 * j + 3] = __uint_as_float(v.y & 0xFFFF0000u);
+                const float4 v = p[j];
+                f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+            }
+        } else {
+            const uint4 *p = reinterpret_cast<const uint4 *>(row + k0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint4 v = p[j];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
+                    f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
+            }
+        }
+    } else if (k0 + 16 <= k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(T) == 4) {
+                const float4 v = reinterpret_cast<const float4 *>(row + k0)[j];
+                f[4 * j + 0] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+            } else {
+                const uint2 v = reinterpret_cast<const uint2 *>(row + k0)[j];
+                f[4 * j + 0] = __uint_as_float(v.x << 16);
+                f[4 * j + 1] = __uint_as_float(v.x & 0xFFFF0000u);
+                f[4 * j + 2] = __uint_as_float(v.y << 16);
+                f[4 * j + 3] = __uint_as_float(v.y & 0xFFFF0000u);
             }
         }
     } else {
@@ -128,16 +127,50 @@ __device__ inline void load_group(const T *row, int64_t k, int64_t g, float f[16
     }
 }
 
-// clamp(rint(v * inv), -127, 127) -- the per-token int8 code
-__device__ inline int quant_i8(float v, float inv)
+// Per-token int8 code q = clamp(rint(v * inv), -127, 127), with inv = 127 / s and
+// s >= max|v|. Since |v * inv| <= 127 * (1 + 2^-23) after rounding, rint never
+// leaves [-127, 127] and the clamp cannot bind. The rounding is done by adding
+// 1.5 * 2^23: the sum has a unit ulp, so the add itself rounds to the nearest
+// integer with ties to even (exactly rint), and the low byte of the float's bits
+// is then the two's-complement int8 code. The multiply and the add are two
+// separately rounded operations (no FMA contraction in this build).
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ inline uint32_t quant_bits(float v, float inv) { return __float_as_uint(v * inv + kRoundMagic); }
+
+__device__ inline int quant_i8(float v, float inv) { return (int)(int8_t)(quant_bits(v, inv) & 0xFFu); }
+
+// Low bytes of four quant_bits() results -> one dword (a in byte 0 ... d in byte 3).
+__device__ inline uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
-    float r = __builtin_rintf(v * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // bytes: a0, b0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // bytes: 0, 0, c0, d0
+    return lo | hi;
 }
 
-// Packs the 16 codes of a group into the qperm byte order (4x4 transpose):
-// dword i = bytes (q[i], q[4+i], q[8+i], q[12+i]).
+// Quantizes the 16 inputs of one group; writes the qperm order (4x4 byte
+// transpose: dword i = codes of inputs i, 4+i, 8+i, 12+i) and/or the natural
+// order, and returns the sum of the 16 codes.
+__device__ inline int quant_group(const float f[16], float inv, uint4 *perm_out, uint4 *nat_out)
+{
+    uint32_t b[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) b[j] = quant_bits(f[j], inv);
+    uint32_t pd[4], nd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pd[i] = pack_low_bytes(b[i], b[4 + i], b[8 + i], b[12 + i]);
+        nd[i] = pack_low_bytes(b[4 * i], b[4 * i + 1], b[4 * i + 2], b[4 * i + 3]);
+    }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum = __builtin_amdgcn_sdot4((int)pd[i], 0x01010101, sum, false);
+    if (perm_out) *perm_out = make_uint4(pd[0], pd[1], pd[2], pd[3]);
+    if (nat_out) *nat_out = make_uint4(nd[0], nd[1], nd[2], nd[3]);
+    return sum;
+}
+
+// Packs 16 codes into the qperm byte order (used where codes are already ints).
 __device__ inline uint4 qperm_pack(const int q[16])
 {
     uint32_t d[4];
@@ -145,17 +178,6 @@ __device__ inline uint4 qperm_pack(const int q[16])
     for (int i = 0; i < 4; ++i)
         d[i] = (uint32_t)(q[i] & 0xFF) | ((uint32_t)(q[4 + i] & 0xFF) << 8) |
                ((uint32_t)(q[8 + i] & 0xFF) << 16) | ((uint32_t)(q[12 + i] & 0xFF) << 24);
-    return make_uint4(d[0], d[1], d[2], d[3]);
-}
-
-// Natural byte order of the same 16 codes.
-__device__ inline uint4 qnat_pack(const int q[16])
-{
-    uint32_t d[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        d[i] = (uint32_t)(q[4 * i] & 0xFF) | ((uint32_t)(q[4 * i + 1] & 0xFF) << 8) |
-               ((uint32_t)(q[4 * i + 2] & 0xFF) << 16) | ((uint32_t)(q[4 * i + 3] & 0xFF) << 24);
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 

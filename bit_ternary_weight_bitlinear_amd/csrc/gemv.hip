@@ -1,26 +1,37 @@
 // gemv.hip -- decode-time BitLinear (m <= 4 tokens) for gfx950.
 //
 // The W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端) at small m is a
-// stream over the packed weights: 2 bits per weight is the whole HBM traffic,
-// so the kernel is built to keep every CU's loads in flight:
-//  * each thread first issues all of its 16-byte non-temporal loads of packed
-//    weights (up to 8 per matrix), before doing anything else;
-//  * while they are in flight, the workgroup quantizes the m tokens itself
-//    (absmax with DPP wave reductions, then rint) into LDS in the qperm order,
-//    so there is no separate activation kernel and no launch gap;
-//  * the codes are decoded in registers with four AND masks and one shift per
-//    dword (code<<0, <<2, <<4 and, after a right shift by one, <<5 -- all fit in
-//    a signed byte) and fed to v_dot4_i32_i8 against the qperm dwords; the
-//    four partial sums are rescaled by exact shifts at the end;
-//  * a row is split over `lpr` lanes (a power of two), reduced with lane shuffles.
-// Integer sums are exact, so the result is independent of the lane split.
+// stream over the packed weights: 2 bits per weight is the whole HBM traffic.
+// Design:
+//  * one workgroup per CU: workgroup b owns rows [b*R, b*R + R) with
+//    R = ceil(n / 256), a contiguous block of R * k/4 bytes, cut into 16-byte
+//    tasks (64 weights of one row) handed to the 512 threads round-robin, row
+//    index fastest. Every CU reads the same number of bytes, and every CU does
+//    the activation quantization below exactly once;
+//  * each thread first issues its activation loads, then all of its weight
+//    loads (a compile-time count, no branches), so everything is in flight at
+//    once and the quantization can start as soon as the activations arrive;
+//  * the workgroup quantizes the m tokens itself (absmax with DPP wave
+//    reductions, round by the 1.5*2^23 add) into LDS in the qperm order: no
+//    separate activation kernel, no launch gap;
+//  * codes are decoded in registers with four AND masks and one shift per
+//    dword (code<<0, <<2, <<4 and, after a right shift by one, <<5 -- each fits a
+//    signed byte) and fed to v_dot4_i32_i8 against the qperm dwords; the four
+//    partial sums are brought back to scale by exact shifts;
+//  * per-task sums are added into per-row int32 accumulators in LDS
+//    (ds_add_u32); integer sums are exact, so the order of the adds does not
+//    matter and the result is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace bl {
 
-constexpr int kMaxChunks = 8;       // 16-byte chunks per thread and matrix
+constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
+constexpr int kMaxTasks = 16;         // 16-byte weight tasks per thread and matrix
 constexpr int kGemvLdsLimit = 60 * 1024;
+constexpr int kSlots = 4;             // activation groups a thread keeps in registers
+constexpr int kGT = 512;              // threads per workgroup (8 waves: two per SIMD)
+constexpr int kGW = kGT / 64;         // waves per workgroup
 
 struct GemvArgs {
     const void *x;
@@ -32,58 +43,115 @@ struct GemvArgs {
     int32_t *acc_out;
     int8_t *q_out;
     float *s_out;
-    int lpr_log2, nch, chunks;
+    int rows_per_wg;  // R
+    int chunks;       // kp / 64
 };
 
-// LDS slot of group (c, d): 16-byte slots rotated by (c >> 2) & 3 so that the
-// lanes of one row, which read neighbouring chunks, spread over the banks.
+// LDS slot of activation group (c, d): 16-byte slots rotated by (c >> 2) & 3 so
+// that lanes reading neighbouring chunks spread over the banks.
 __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) & 3)) << 4); }
 
-template <typename T, bool VEC, int MT, bool DUAL>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a)
+// RES: all m*ceil(k/16) activation groups fit in kSlots per thread (loaded once,
+// quantized from registers). FULL: k % 16 == 0. JM: weight tasks per thread.
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM>
+__global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
-    extern __shared__ __align__(16) int8_t q_lds[];  // [MT][kp]
-    __shared__ float red_f[MT][4];
-    __shared__ int red_i[MT][4];
+    constexpr int NA = DUAL ? 2 : 1;
+    extern __shared__ __align__(16) int8_t lds[];  // q [MT][kp], then int32 sums [NA][MT][R]
+    __shared__ float red_f[MT][kGW];
+    __shared__ int red_i[MT][kGW];
+    int8_t *q_lds = lds;
+    int *acc_lds = reinterpret_cast<int *>(lds + MT * a.kp);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int lpr = 1 << a.lpr_log2;
-    const int p = tid & (lpr - 1);
-    const int64_t row = (int64_t)blockIdx.x * (kThreads >> a.lpr_log2) + (tid >> a.lpr_log2);
-    const bool row_ok = row < a.n;
+    const int R = a.rows_per_wg, C = a.chunks;
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
+    const int ntask = rows * C;
+    const T *x = static_cast<const T *>(a.x);
+    const int G = (int)ceil_div(a.k, 16);
+    const int GP = (int)(a.kp / 16);
+    const int NG = MT * G;
 
-    // 1. issue every packed-weight load of this thread
-    uint4 wa[kMaxChunks], wb[kMaxChunks];
-    {
-        const uint4 *pa = reinterpret_cast<const uint4 *>(a.w0 + (row_ok ? row : 0) * a.ldw);
-        const uint4 *pb = reinterpret_cast<const uint4 *>((DUAL ? a.w1 : a.w0) + (row_ok ? row : 0) * a.ldw);
+    // 1. activation loads first: the quantization waits only for these
+    float xr[kSlots][16];
+    int slot_t[kSlots], slot_g[kSlots];
+    if constexpr (RES) {
 #pragma unroll
-        for (int j = 0; j < kMaxChunks; ++j) {
-            const int c = p + (j << a.lpr_log2);
-            const bool ok = row_ok && j < a.nch && c < a.chunks;
-            wa[j] = ok ? load_nt16(pa + c) : make_uint4(0, 0, 0, 0);
-            if constexpr (DUAL) wb[j] = ok ? load_nt16(pb + c) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < kSlots; ++s) {
+            const int f = min(tid + s * kGT, NG - 1);  // clamped: always a valid group
+            slot_t[s] = MT == 1 ? 0 : f / G;
+            slot_g[s] = f - slot_t[s] * G;
+            if (s * kGT < NG)  // uniform: slots no thread needs are not loaded
+                load_group<T, FULL>(x + slot_t[s] * a.k, a.k, slot_g[s], xr[s]);
         }
     }
 
-    // 2. per-token absmax quantization of the MT tokens into LDS
-    const T *x = static_cast<const T *>(a.x);
-    const int64_t G = ceil_div(a.k, 16);
-    const int GP = (int)(a.kp / 16);
+    // 2. the weight tasks of this thread: task f = tid + 256*j is (row f % rows,
+    //    chunk f / rows); tasks past the end repeat the last one (sums dropped)
+    int tr[JM], tc[JM];
+    {
+        const int last = ntask - 1;
+        const int lc = last / rows, lr = last - lc * rows;
+        const int dc = kGT / rows, dr = kGT - dc * rows;
+        int c = tid / rows;
+        int r = tid - c * rows;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const bool ok = tid + j * kGT < ntask;
+            tr[j] = ok ? r : lr;
+            tc[j] = ok ? c : lc;
+            r += dr;
+            c += dc;
+            if (r >= rows) {
+                r -= rows;
+                c += 1;
+            }
+        }
+    }
+    uint4 wa[JM], wb[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int64_t off = (r0 + tr[j]) * a.ldw + (int64_t)tc[j] * 16;
+        wa[j] = load_nt16(a.w0 + off);
+        if constexpr (DUAL) wb[j] = load_nt16(a.w1 + off);
+    }
+    // keep every load above this point in issue order: nothing below may be
+    // hoisted between them, so all of this thread's reads are in flight at once
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. per-token absmax, then int8 codes into LDS in the qperm order
     float st[MT], inv[MT];
     int sq[MT];
     {
         float amax[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            amax[t] = 0.0f;
-            for (int64_t g = tid; g < G; g += kThreads) {
-                float f[16];
-                load_group<T, VEC>(x + t * a.k, a.k, g, f);
+        for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
+        if constexpr (RES) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) amax[t] = fmaxf(amax[t], fabsf(f[j]));
+            for (int s = 0; s < kSlots; ++s) {
+                if (s * kGT < NG) {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(xr[s][j]));
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        if (slot_t[s] == t) amax[t] = fmaxf(amax[t], m);
+                }
             }
+        } else {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                for (int g = tid; g < G; g += kGT) {
+                    float f[16];
+                    load_group<T, FULL>(x + t * a.k, a.k, g, f);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) amax[t] = fmaxf(amax[t], fabsf(f[j]));
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
             amax[t] = wave_max(amax[t]);
             if (lane == 0) red_f[t][wave] = amax[t];
         }
@@ -91,56 +159,88 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a)
         int qs[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            st[t] = fmaxf(fmaxf(fmaxf(red_f[t][0], red_f[t][1]), fmaxf(red_f[t][2], red_f[t][3])), kEps);
+            float mx = red_f[t][0];
+#pragma unroll
+            for (int w = 1; w < kGW; ++w) mx = fmaxf(mx, red_f[t][w]);
+            st[t] = fmaxf(mx, kEps);
             inv[t] = 127.0f / st[t];
             qs[t] = 0;
-            for (int g = tid; g < GP; g += kThreads) {
-                float f[16];
-                if (g < G) {
-                    load_group<T, VEC>(x + t * a.k, a.k, g, f);
-                } else {
+        }
+        auto emit = [&](int t, int g, const float f[16], float iv) {
+            uint4 pv, nv;
+            const int sum = quant_group(f, iv, &pv, &nv);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) f[j] = 0.0f;
-                }
-                int qi[16];
+            for (int u = 0; u < MT; ++u)
+                if (u == t) qs[u] += sum;
+            *reinterpret_cast<uint4 *>(q_lds + t * a.kp + lds_slot(g >> 2, g & 3)) = pv;
+            if (a.q_out && blockIdx.x == 0) {
+                const uint32_t dw[4] = {nv.x, nv.y, nv.z, nv.w};
+                uint32_t *dst = reinterpret_cast<uint32_t *>(a.q_out + t * a.k + 16 * (int64_t)g);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    qi[j] = quant_i8(f[j], inv[t]);
-                    qs[t] += qi[j];
-                }
-                const int c = g >> 2, d = g & 3;
-                *reinterpret_cast<uint4 *>(q_lds + t * a.kp + lds_slot(c, d)) = qperm_pack(qi);
-                if (a.q_out && blockIdx.x == 0 && g < G) {
-                    const uint4 v = qnat_pack(qi);
-                    const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
-                    uint32_t *dst = reinterpret_cast<uint32_t *>(a.q_out + t * a.k + 16 * (int64_t)g);
+                for (int j = 0; j < 4; ++j)
+                    if (16 * (int64_t)g + 4 * j < a.k) dst[j] = dw[j];
+            }
+        };
+        if constexpr (RES) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * (int64_t)g + 4 * j < a.k) dst[j] = dw[j];
+            for (int s = 0; s < kSlots; ++s) {
+                if (tid + s * kGT < NG) {
+                    float iv = inv[0];
+#pragma unroll
+                    for (int t = 1; t < MT; ++t)
+                        if (slot_t[s] == t) iv = inv[t];
+                    emit(slot_t[s], slot_g[s], xr[s], iv);
                 }
             }
+        } else {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                for (int g = tid; g < G; g += kGT) {
+                    float f[16];
+                    load_group<T, FULL>(x + t * a.k, a.k, g, f);
+                    emit(t, g, f, inv[t]);
+                }
+        }
+        // zero inputs of the padding up to kp, and the row accumulators
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            for (int g = G + tid; g < GP; g += kGT)
+                *reinterpret_cast<uint4 *>(q_lds + t * a.kp + lds_slot(g >> 2, g & 3)) = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < NA * MT * R; i += kGT) acc_lds[i] = 0;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
             qs[t] = wave_sum(qs[t]);
             if (lane == 0) red_i[t][wave] = qs[t];
             if (a.s_out && blockIdx.x == 0 && tid == 0) a.s_out[t] = st[t];
         }
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < MT; ++t) sq[t] = red_i[t][0] + red_i[t][1] + red_i[t][2] + red_i[t][3];
+        for (int t = 0; t < MT; ++t) {
+            sq[t] = 0;
+#pragma unroll
+            for (int w = 0; w < kGW; ++w) sq[t] += red_i[t][w];
+        }
     }
 
-    // 3. decode the 2-bit codes in registers, v_dot4 against the qperm dwords
-    int acc[MT][4], accb[MT][4];
+    // 4. decode the 2-bit codes in registers, v_dot4 against the qperm dwords,
+    //    add each task's sum into its row's LDS accumulator
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int j = 0; j < JM; ++j) {
+        if (tid + j * kGT < ntask) {
+            const int c = tc[j];
+            int acc[MT][4], accb[MT][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = accb[t][i] = 0;
-
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-        const int c = p + (j << a.lpr_log2);
-        if (j < a.nch && c < a.chunks) {
+                for (int i = 0; i < 4; ++i) acc[t][i] = accb[t][i] = 0;
             const uint32_t wda[4] = {wa[j].x, wa[j].y, wa[j].z, wa[j].w};
-            const uint32_t wdb[4] = {wb[j].x, wb[j].y, wb[j].z, wb[j].w};
+            uint32_t wdb[4] = {0, 0, 0, 0};
+            if constexpr (DUAL) {
+                wdb[0] = wb[j].x;
+                wdb[1] = wb[j].y;
+                wdb[2] = wb[j].z;
+                wdb[3] = wb[j].w;
+            }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const int e0 = (int)(wda[d] & 0x03030303u);
@@ -169,49 +269,135 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a)
                     }
                 }
             }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                // undo the field shifts (each partial is an exact multiple)
+                atomicAdd(&acc_lds[t * R + tr[j]],
+                          acc[t][0] + (acc[t][1] >> 2) + (acc[t][2] >> 4) + (acc[t][3] >> 5));
+                if constexpr (DUAL)
+                    atomicAdd(&acc_lds[(MT + t) * R + tr[j]],
+                              accb[t][0] + (accb[t][1] >> 2) + (accb[t][2] >> 4) + (accb[t][3] >> 5));
+            }
         }
     }
+    __syncthreads();
 
-    // 4. undo the field shifts, reduce over the lanes of the row, rescale
+    // 5. rescale: y = (float)acc * ((s / 127) * gamma); the pair gives h = relu(g)^2 * u
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        int ta = acc[t][0] + (acc[t][1] >> 2) + (acc[t][2] >> 4) + (acc[t][3] >> 5);
-        int tb = accb[t][0] + (accb[t][1] >> 2) + (accb[t][2] >> 4) + (accb[t][3] >> 5);
-        for (int off = lpr >> 1; off > 0; off >>= 1) {
-            ta += __shfl_xor(ta, off);
-            if constexpr (DUAL) tb += __shfl_xor(tb, off);
-        }
-        if (p == 0 && row_ok) {
-            const int va = ta - sq[t];
-            const float ya = (float)va * token_scale(st[t], a.gamma0[0]);
+        const float ca = token_scale(st[t], a.gamma0[0]);
+        const float cb = DUAL ? token_scale(st[t], a.gamma1[0]) : 0.0f;
+        for (int r = tid; r < rows; r += kGT) {
+            const int va = acc_lds[t * R + r] - sq[t];
+            const float ya = (float)va * ca;
+            float *o = a.out + t * a.n + r0 + r;
             if constexpr (DUAL) {
-                const int vb = tb - sq[t];
-                const float yb = (float)vb * token_scale(st[t], a.gamma1[0]);
-                a.out[t * a.n + row] = sq_relu_gate(ya, yb);
+                const int vb = acc_lds[(MT + t) * R + r] - sq[t];
+                *o = sq_relu_gate(ya, (float)vb * cb);
             } else {
-                a.out[t * a.n + row] = ya;
-                if (a.acc_out) a.acc_out[t * a.n + row] = va;
+                *o = ya;
+                if (a.acc_out) a.acc_out[t * a.n + r0 + r] = va;
             }
         }
     }
 }
 
+// ---------------------------------------------------------------- host side
+
+// Rows per workgroup: one workgroup per CU while that keeps each thread at <= 4
+// weight loads (counting both matrices of a gate/up pair); larger matrices are
+// split further so more workgroups share a CU and hide each other's latency.
+constexpr int kTargetLoads = 4;
+
+static int64_t gemv_rows_per_wg(int64_t n, int64_t chunks, bool dual)
+{
+    int64_t r = ceil_div(n, kNumCUs);
+    const int64_t na = dual ? 2 : 1;
+    while (r > 1 && r * chunks * na > (int64_t)kTargetLoads * kGT) r = ceil_div(r, 2);
+    const int64_t rmax = (int64_t)kMaxTasks * kGT / chunks;  // tasks per thread <= 16
+    if (r > rmax) r = rmax;
+    return r < 1 ? 1 : r;
+}
+
+static size_t gemv_lds_bytes(int64_t m, int64_t kp, int64_t r, bool dual)
+{
+    return (size_t)(m * kp + (dual ? 2 : 1) * m * r * 4);
+}
+
 bool gemv_supported(int64_t m, int64_t kp)
 {
     const int64_t chunks = kp / 64;
-    return m >= 1 && m <= 4 && m * kp <= kGemvLdsLimit && chunks <= 64 * kMaxChunks;
+    if (m < 1 || m > 4 || chunks > (int64_t)kMaxTasks * kGT) return false;
+    // worst case over n: rows per workgroup is at most 16*256/chunks
+    const int64_t rmax = (int64_t)kMaxTasks * kGT / chunks;
+    return gemv_lds_bytes(m, kp, rmax, true) <= (size_t)kGemvLdsLimit;
 }
 
-template <typename T, bool VEC, bool DUAL>
-static void launch_mt(int mt, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+namespace {
+
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM>
+void launch_one(dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM>), grid, dim3(kGT), lds, st, a);
+}
+
+// single token, whole groups, activations resident: the decode hot path, with
+// the task count per thread matched closely
+template <typename T, bool DUAL>
+void launch_m1(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    if (jm <= 1) launch_one<T, 1, DUAL, true, true, 1>(grid, lds, st, a);
+    else if (jm <= 2) launch_one<T, 1, DUAL, true, true, 2>(grid, lds, st, a);
+    else if (jm <= 3) launch_one<T, 1, DUAL, true, true, 3>(grid, lds, st, a);
+    else if (jm <= 4) launch_one<T, 1, DUAL, true, true, 4>(grid, lds, st, a);
+    else if (jm <= 5) launch_one<T, 1, DUAL, true, true, 5>(grid, lds, st, a);
+    else if (jm <= 6) launch_one<T, 1, DUAL, true, true, 6>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<T, 1, DUAL, true, true, 8>(grid, lds, st, a);
+    else if (jm <= 10) launch_one<T, 1, DUAL, true, true, 10>(grid, lds, st, a);
+    else if (jm <= 12) launch_one<T, 1, DUAL, true, true, 12>(grid, lds, st, a);
+    else if (jm <= 14) launch_one<T, 1, DUAL, true, true, 14>(grid, lds, st, a);
+    else launch_one<T, 1, DUAL, true, true, 16>(grid, lds, st, a);
+}
+
+// 2..4 tokens, whole groups, activations resident
+template <typename T, int MT, bool DUAL>
+void launch_mt(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    if (jm <= 4) launch_one<T, MT, DUAL, true, true, 4>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<T, MT, DUAL, true, true, 8>(grid, lds, st, a);
+    else launch_one<T, MT, DUAL, true, true, 16>(grid, lds, st, a);
+}
+
+// anything else (k % 16 != 0, or activations too long for registers)
+template <typename T, bool DUAL>
+void launch_generic(int mt, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
     switch (mt) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<T, VEC, 1, DUAL>), grid, dim3(kThreads), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<T, VEC, 2, DUAL>), grid, dim3(kThreads), lds, st, a); break;
-    case 3: hipLaunchKernelGGL((gemv_kernel<T, VEC, 3, DUAL>), grid, dim3(kThreads), lds, st, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<T, VEC, 4, DUAL>), grid, dim3(kThreads), lds, st, a); break;
+    case 1: launch_one<T, 1, DUAL, false, false, 16>(grid, lds, st, a); break;
+    case 2: launch_one<T, 2, DUAL, false, false, 16>(grid, lds, st, a); break;
+    case 3: launch_one<T, 3, DUAL, false, false, 16>(grid, lds, st, a); break;
+    default: launch_one<T, 4, DUAL, false, false, 16>(grid, lds, st, a); break;
     }
 }
+
+template <typename T, bool DUAL>
+void dispatch(const GemvProblem &p, int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    const bool res = p.m * ceil_div(p.k, 16) <= (int64_t)kSlots * kGT;
+    const bool full = p.k % 16 == 0;
+    if (!res || !full) {
+        launch_generic<T, DUAL>((int)p.m, grid, lds, st, a);
+        return;
+    }
+    switch (p.m) {
+    case 1: launch_m1<T, DUAL>(jm, grid, lds, st, a); break;
+    case 2: launch_mt<T, 2, DUAL>(jm, grid, lds, st, a); break;
+    case 3: launch_mt<T, 3, DUAL>(jm, grid, lds, st, a); break;
+    default: launch_mt<T, 4, DUAL>(jm, grid, lds, st, a); break;
+    }
+}
+
+}  // namespace
 
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
 {
@@ -221,36 +407,18 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out; a.q_out = p.q_out; a.s_out = p.s_out;
     a.chunks = (int)(p.kp / 64);
-
-    // lanes per row: the fewest that keep <= 8 chunks per lane, then more lanes
-    // while the grid is smaller than the chip and the lanes stay >= 75 % busy
-    int lg = 0;
-    while (ceil_div(a.chunks, 1 << lg) > kMaxChunks) ++lg;
-    while (lg < 6) {
-        const int64_t blocks = ceil_div(p.n, kThreads >> lg);
-        const int nlg = lg + 1;
-        const int64_t nch2 = ceil_div(a.chunks, 1 << nlg);
-        const double eff = (double)a.chunks / (double)(nch2 << nlg);
-        if (blocks >= 256 || eff < 0.75) break;
-        lg = nlg;
-    }
-    a.lpr_log2 = lg;
-    a.nch = (int)ceil_div(a.chunks, 1 << lg);
-    const dim3 grid((unsigned)ceil_div(p.n, kThreads >> lg));
-    const size_t lds = (size_t)(p.m * p.kp);
     const bool dual = p.w1 != nullptr;
+    const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);
+    a.rows_per_wg = (int)r;
+    const int jm = (int)ceil_div(r * a.chunks, kGT);
+    const dim3 grid((unsigned)ceil_div(p.n, r));
+    const size_t lds = gemv_lds_bytes(p.m, p.kp, r, dual);
     if (p.bf16) {
-        const bool vec = p.k % 8 == 0;
-        if (dual) {
-            if (vec) launch_mt<bf16_t, true, true>((int)p.m, grid, lds, st, a);
-            else launch_mt<bf16_t, false, true>((int)p.m, grid, lds, st, a);
-        } else {
-            if (vec) launch_mt<bf16_t, true, false>((int)p.m, grid, lds, st, a);
-            else launch_mt<bf16_t, false, false>((int)p.m, grid, lds, st, a);
-        }
+        if (dual) dispatch<bf16_t, true>(p, jm, grid, lds, st, a);
+        else dispatch<bf16_t, false>(p, jm, grid, lds, st, a);
     } else {
-        if (dual) launch_mt<float, true, true>((int)p.m, grid, lds, st, a);
-        else launch_mt<float, true, false>((int)p.m, grid, lds, st, a);
+        if (dual) dispatch<float, true>(p, jm, grid, lds, st, a);
+        else dispatch<float, false>(p, jm, grid, lds, st, a);
     }
     return hipGetLastError();
 }

@@ -80,6 +80,7 @@ def test_quant_act_zero_token(bl):
 
 FWD_SHAPES = [
     (1, 4, 1), (1, 256, 256), (2, 260, 7), (3, 2560, 300), (4, 1024, 129),      # decode path
+    (1, 2560, 6913), (3, 512, 1031), (1, 16384, 300), (2, 20000, 64),            # decode: ragged blocks, long k
     (5, 256, 256), (17, 260, 33), (33, 512, 257), (64, 2560, 512), (65, 256, 300),  # MFMA paths
     (130, 640, 200), (300, 256, 130),
 ]
@@ -206,3 +207,34 @@ def test_workload_ffn_8b_decode(bl):
 
 def test_workload_ffn_8b_prefill(bl):
     _ffn_case(bl, 5, 2048, 4096, 14336, sample=np.array([0, 1, 255, 256, 1023, 2047]))
+
+
+# ------------------------------------------------------------------ HIP graph capture
+
+@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (3, 1024, 300), (64, 2560, 512), (300, 512, 640)])
+def test_graph_replay_matches_eager(bl, m, k, n):
+    """The library enqueues only kernels (no allocation, no memset), so a captured
+    forward must reproduce the eager result on every replay."""
+    w, _, _, _ = make_linear(97, 1, n, k)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    x = to_dev(synth.activations(97, m, k, dtype="bf16"), "bf16")
+    ws_bytes = bl.workspace_size(bl.OP_FORWARD, m, k, n)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    eager = host(bl.forward(x, packed, gamma, workspace=ws if ws_bytes else None)).copy()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.forward(x, packed, gamma, out=y, workspace=ws if ws_bytes else None)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        bl.forward(x, packed, gamma, out=y, workspace=ws if ws_bytes else None)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y).view(np.uint32), eager.view(np.uint32), err_msg=f"replay {rep}")
+        # unrelated eager work on the same buffers between replays
+        bl.forward(x * 2, packed, gamma, out=y, workspace=ws if ws_bytes else None)
+        torch.cuda.synchronize()
