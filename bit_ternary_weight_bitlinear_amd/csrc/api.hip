@@ -209,7 +209,7 @@ bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k, cons
     g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
     g.out = y; g.acc_out = acc_out; g.epi = EPI_Y;
-    return hip_status(launch_gemm(g, st));
+    return hip_status(launch_contraction(g, st));
 }
 
 bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
@@ -234,7 +234,7 @@ bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_
     g.qp = L.qp; g.kp = L.kp; g.s = nullptr; g.sumq = L.sumq; g.m = m; g.n = n;
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = nullptr; g.gamma1 = nullptr;
     g.out = nullptr; g.acc_out = acc; g.epi = EPI_ACC;
-    return hip_status(launch_gemm(g, st));
+    return hip_status(launch_contraction(g, st));
 }
 
 bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int64_t ffn,
@@ -286,7 +286,7 @@ bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int
     g.qp = L.qx; g.kp = L.hp; g.s = L.sx; g.sumq = L.sumx; g.m = m; g.n = ffn;
     g.w0 = wg; g.w1 = wu; g.ldw = L.hp / 4; g.gamma0 = gate_gamma; g.gamma1 = up_gamma;
     g.out = L.h; g.acc_out = nullptr; g.epi = EPI_GATE;
-    if (hipError_t e = launch_gemm(g, st)) return hip_status(e);
+    if (hipError_t e = launch_contraction(g, st)) return hip_status(e);
     float *sh = hs_out ? hs_out : L.sh;  // the requantization scales go straight to hs_out if asked
     if (hipError_t e = launch_act_quant(L.h, false, m, ffn, L.fp, hq_out, L.qh, sh, L.sumh, st))
         return hip_status(e);
@@ -294,7 +294,7 @@ bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int
     d.qp = L.qh; d.kp = L.fp; d.s = sh; d.sumq = L.sumh; d.m = m; d.n = hidden;
     d.w0 = wd; d.w1 = nullptr; d.ldw = L.fp / 4; d.gamma0 = down_gamma; d.gamma1 = nullptr;
     d.out = y; d.acc_out = nullptr; d.epi = EPI_Y;
-    return hip_status(launch_gemm(d, st));
+    return hip_status(launch_contraction(d, st));
 }
 
 }  // extern "C"

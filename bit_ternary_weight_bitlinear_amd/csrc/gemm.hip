@@ -1,23 +1,47 @@
-// gemm.hip -- BitLinear at m > 4 tokens on the gfx950 int8 matrix cores.
+// gemm.hip -- BitLinear at m > 64 tokens on the gfx950 int8 matrix cores.
 //
 // At many tokens the W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端)
-// is a dense contraction, so it runs on v_mfma_i32_32x32x32_i8:
-//  * A operand = weights. Each k-step, the workgroup loads its BN packed rows
-//    (16 bytes = 64 weights per row), expands the 2-bit codes to int8 in
-//    registers ((w >> 2i) & 0x03030303 gives the codes of inputs 16g+4b+i, i.e.
-//    exactly the qperm byte order) and writes the int8 tile to LDS.
-//  * B operand = qperm activations, copied to LDS as they are.
-//  * Codes are w+1 in {0,1,2}; the epilogue subtracts sum_k q per token.
-//  * C[n][m] per 32x32 block: lane l holds n = 8*(v/4) + 4*(l/32) + v%4 and
-//    m = l%32, so every lane stores 4 consecutive outputs of one token (16 B).
-// Integer accumulation is exact; the fp32 rescale matches the decode path bit
-// for bit.
+// is a dense contraction, so it runs on v_mfma_i32_32x32x32_i8 with the
+// activations as operand A and the ternary codes as operand B:
+//  * a workgroup (4 waves) owns a tile of 128*FM tokens x 32*FN output
+//    features; wave w takes tokens [32*FM*w, 32*FM*(w+1)) of it against all
+//    32*FN features (FM*FN accumulator blocks of 32x32);
+//  * two LDS rings, filled by direct global->LDS loads (global_load_lds_dwordx4)
+//    issued DB k-steps ahead: the qperm activation tile of each 64-input step
+//    (64-byte rows) and the packed weight rows of that step (16-byte rows).
+//    The loads take a scalar base (advanced by one step with scalar adds) and
+//    a constant per-lane offset, and ring positions are scalar offsets, so the
+//    loop spends its vector instructions on the weight expansion alone;
+//  * the weights stay packed in LDS. Each lane reads the 8 packed bytes its
+//    operand needs for a whole step (one ds_read_b64) and expands them in
+//    registers: (w >> 2i) & 0x03030303 holds the codes of inputs 16g+4b+i,
+//    exactly the qperm byte order of the activations. Lanes 0-31 take 16-input
+//    groups {0,1} of the step, lanes 32-63 groups {2,3}: half-step h uses
+//    group h + 2*(lane/32) on both operands;
+//  * software pipelined by half steps: while one half's MFMAs run, the wave
+//    reads the other half's activation fragments and the next step's packed
+//    weights; one barrier per step, which waits only for the direct loads the
+//    next step reads (the younger ones stay in flight across it). Two steps per
+//    loop iteration let the packed-weight registers alternate without copies;
+//  * the tile's per-token sum_k q and s arrive in LDS by direct loads in the
+//    prologue and are read back four tokens at a time by the epilogue;
+//  * activation rows are 64 bytes (four 16-byte slots), slot index XORed by
+//    (row >> 2) & 3, so the sixteen lanes of each ds_read_b128 phase, reading
+//    sixteen consecutive rows at one slot, cover all 64 banks once;
+//  * tiles are ordered per XCD: workgroup i runs on XCD i % 8, so XCD x gets a
+//    contiguous range of tiles that share their activation rows (L2 reuse);
+//  * accumulator block layout: lane l holds feature n = l % 32 and tokens
+//    m = 8*(v/4) + 4*(l/32) + v%4 in register v, so each store instruction
+//    writes two 128-byte row segments;
+//  * codes are w+1 in {0,1,2}; the epilogue subtracts sum_k q per token.
+// Integer accumulation is exact; the fp32 rescale is the same operation
+// sequence as on the decode path.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace bl {
-
-constexpr int kLdsStride = 80;  // bytes per 64-byte tile row (16 bytes of padding)
 
 struct GemmArgs {
     const int8_t *qp;
@@ -30,173 +54,387 @@ struct GemmArgs {
     const float *gamma0, *gamma1;
     float *out;
     int32_t *acc_out;
+    int n_tiles, m_tiles;
 };
 
-__device__ inline uint4 expand_codes(uint32_t w)
+// byte offset of (row, 16-byte group g) in a 64-byte-row LDS tile
+__device__ inline int tile_off(int row, int g) { return row * 64 + ((g ^ ((row >> 2) & 3)) << 4); }
+
+// Direct loads from global memory into LDS with a scalar base address and a
+// per-lane 32-bit byte offset. Lane i of the wave writes LDS byte address
+// lds + 16*i (lds + 4*i for the dword form); lds must be wave-uniform. Issued
+// as inline asm so that the only waits on these loads are the explicit ones in
+// ring_barrier(): the compiler would otherwise drain every in-flight direct
+// load before any LDS read. No VGPR is written by them.
+// a wave-uniform 64-bit address as a scalar operand
+__device__ inline uint64_t uniform_ptr(const void *p)
 {
-    return make_uint4(w & 0x03030303u, (w >> 2) & 0x03030303u, (w >> 4) & 0x03030303u,
-                      (w >> 6) & 0x03030303u);
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-template <int BN, int BM, int WN, int WM, int EPI>
+__device__ inline void dma16(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+__device__ inline void dma4(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+// LDS byte address of a pointer into the workgroup's LDS
+__device__ inline uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// s_waitcnt immediate: vmcnt <= VM, lgkmcnt = 0, expcnt untouched (gfx9 encoding)
+template <int VM>
+constexpr int waitcnt_vm_lgkm0() { return (VM & 15) | (7 << 4) | ((VM >> 4) << 14); }
+
+// Barrier that leaves the newest VM direct loads in flight: wait until at most
+// VM vector-memory operations of this thread are outstanding and all LDS
+// operations are done, then s_barrier. The empty asm statements keep the
+// compiler from moving memory accesses across.
+template <int VM>
+__device__ inline void ring_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VM>());
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ inline v4i expand_b(uint32_t w)
+{
+    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+               (int)((w >> 6) & 0x03030303u)};
+}
+
+template <int FM, int FN, int EPI, int DB>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
     constexpr bool DUAL = EPI == EPI_GATE;
     constexpr int NA = DUAL ? 2 : 1;
-    constexpr int NWN = BN / WN, NWM = BM / WM;
-    static_assert(NWN * NWM == 4, "four waves per workgroup");
-    constexpr int FN = WN / 32, FM = WM / 32;
-    constexpr int A_LD = (BN + kThreads - 1) / kThreads;
-    constexpr int B_LD = (BM * 4 + kThreads - 1) / kThreads;
+    constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
+    static_assert(FM * FN * NA <= 16, "accumulators fit the 256 AGPRs");
+    static_assert(BN <= 256, "packed rows: one 64-row direct load per wave");
+    static_assert(DB >= 3, "at least one step of slack for the direct loads");
+    constexpr int SBX = DB + 1;            // activation stages (steps ks .. ks+DB live)
+    constexpr int SBW = DB;                // packed-weight stages (steps ks+1 .. ks+DB live)
+    constexpr int X_TILE = BM * 64;        // activation bytes per step
+    constexpr int W_PK = 256 * 16;         // packed bytes per step and matrix (256 rows)
+    constexpr int W_STAGE = NA * W_PK;
+    constexpr int X_INSTR = BM / 64;       // activation direct loads per thread per step
+    constexpr int DPS = X_INSTR + NA;      // direct loads per thread per step
+    constexpr int VM_SLACK = (DB - 2) * DPS;
+    static_assert(VM_SLACK < 64, "vmcnt field");
+    // LDS: xring[SBX][X_TILE], wring[SBW][NA][W_PK], then sum_k q and s of the tile's tokens
+    constexpr int XR = 0, WR = SBX * X_TILE, TQ = WR + SBW * W_STAGE, TS = TQ + BM * 4;
+    extern __shared__ __align__(16) int8_t smem[];
+    const uint32_t lds0 = lds_addr(smem);
 
-    __shared__ __align__(16) int8_t As[NA][BN * kLdsStride];
-    __shared__ __align__(16) int8_t Bs[BM * kLdsStride];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 31, lhalf = lane >> 5;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % NWN, wm = wave / NWN;
-    const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+    // XCD-aware tile order: workgroups id, id+8, id+16, ... share an XCD and get
+    // consecutive tiles, row-major over (m tile, n tile)
+    const int tiles = a.n_tiles * a.m_tiles;
+    const int id = blockIdx.x, xcd = id & 7, per = tiles >> 3, rem = tiles & 7;
+    const int tile = xcd * per + min(xcd, rem) + (id >> 3);
+    const int64_t m0 = (int64_t)(tile / a.n_tiles) * BM, n0 = (int64_t)(tile % a.n_tiles) * BN;
+    const int nks = (int)(a.kp / 64);
 
-    uint4 ra[NA][A_LD], rb[B_LD];
-    auto gload = [&](int64_t ks) {
+    // direct-load sources: scalar bases advanced per step, constant per-lane offsets
+    const int8_t *xbase = a.qp + m0 * a.kp;
+    uint32_t xoff[X_INSTR];
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int r = tid + i * kThreads;
-            const int64_t n = n0 + r;
-            const bool ok = r < BN && n < a.n;
+    for (int i = 0; i < X_INSTR; ++i) {
+        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+        const int g = (lane & 3) ^ ((row >> 2) & 3);
+        xoff[i] = (uint32_t)(row * a.kp + g * 16);
+    }
+    const uint8_t *wbase[NA];
 #pragma unroll
-            for (int mat = 0; mat < NA; ++mat) {
-                const uint8_t *w = mat == 0 ? a.w0 : a.w1;
-                ra[mat][i] = ok ? *reinterpret_cast<const uint4 *>(w + n * a.ldw + ks * 16)
-                                : make_uint4(0, 0, 0, 0);
-            }
-        }
+    for (int mat = 0; mat < NA; ++mat) wbase[mat] = (mat == 0 ? a.w0 : a.w1) + n0 * a.ldw;
+    uint32_t woff;
+    {
+        // rows past the tile or the matrix re-read a valid row (results dropped)
+        int64_t n = n0 + min(wave * 64 + lane, BN - 1);
+        n = n < a.n ? n : a.n - 1;
+        woff = (uint32_t)((n - n0) * a.ldw);
+    }
+    // requests step j into the stages at byte offsets xo / wo of the rings
+    auto dma_step = [&](int j, uint32_t xo, uint32_t wo) {
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int e = tid + i * kThreads;
-            if (e < BM * 4) {
-                const int r = e >> 2, part = e & 3;
-                rb[i] = *reinterpret_cast<const uint4 *>(a.qp + (m0 + r) * a.kp + ks * 64 + part * 16);
-            }
-        }
+        for (int i = 0; i < X_INSTR; ++i)
+            dma16(xbase + (int64_t)j * 64, xoff[i], lds0 + XR + xo + (i * 4 + wave) * 1024);
+#pragma unroll
+        for (int mat = 0; mat < NA; ++mat)
+            dma16(wbase[mat] + (int64_t)j * 16, woff, lds0 + WR + wo + mat * W_PK + wave * 1024);
     };
-    auto swrite = [&]() {
+
+    // LDS read addresses: per-lane bases, stage offsets added per step
+    const uint32_t xl0 = XR + tile_off(wave * WM + lrow, 2 * lhalf);      // half 0: group 2*lhalf
+    const uint32_t xl1 = XR + tile_off(wave * WM + lrow, 1 + 2 * lhalf);  // half 1: group 1 + 2*lhalf
+    const uint32_t wl = WR + lrow * 16 + lhalf * 8;
+    // fragments fm sit 32 rows (2 KB) apart with the same swizzle: (row >> 2) & 3 depends on row % 16 only
+    auto read_x = [&](uint32_t addr, v4i (&x)[FM]) {
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int r = tid + i * kThreads;
-            if (r < BN) {
+        for (int fm = 0; fm < FM; ++fm) x[fm] = *reinterpret_cast<const v4i *>(smem + addr + fm * 2048);
+    };
+    // packed weights of a step: dwords 2*lhalf and 2*lhalf+1 of each of the tile's rows
+    auto read_w = [&](uint32_t addr, v2u (&w)[NA][FN]) {
 #pragma unroll
-                for (int mat = 0; mat < NA; ++mat) {
-                    const uint32_t wd[4] = {ra[mat][i].x, ra[mat][i].y, ra[mat][i].z, ra[mat][i].w};
+        for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d)
-                        *reinterpret_cast<uint4 *>(&As[mat][r * kLdsStride + d * 16]) = expand_codes(wd[d]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int e = tid + i * kThreads;
-            if (e < BM * 4) {
-                const int r = e >> 2, part = e & 3;
-                *reinterpret_cast<uint4 *>(&Bs[r * kLdsStride + part * 16]) = rb[i];
-            }
-        }
+            for (int fn = 0; fn < FN; ++fn)
+                w[mat][fn] = *reinterpret_cast<const v2u *>(smem + addr + mat * W_PK + fn * 512);
     };
 
-    v16i acc[NA][FN][FM];
+    v16i acc[NA][FM][FN];
 #pragma unroll
     for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mat][fn][fm][v] = 0;
+                for (int v = 0; v < 16; ++v) acc[mat][fm][fn][v] = 0;
 
-    const int64_t nks = a.kp / 64;
-    gload(0);
-    for (int64_t ks = 0; ks < nks; ++ks) {
-        __syncthreads();
-        swrite();
-        __syncthreads();
-        if (ks + 1 < nks) gload(ks + 1);
+    auto mfma_half = [&](const v4i (&x)[FM], const v2u (&w)[NA][FN], auto hc) {
+        constexpr int h = decltype(hc)::value;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int col = (2 * s + (lane >> 5)) * 16;
-            v4i bf[FM];
+        for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                bf[fm] = *reinterpret_cast<const v4i *>(&Bs[(wm * WM + fm * 32 + (lane & 31)) * kLdsStride + col]);
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i b = expand_b(w[mat][fn][h]);
 #pragma unroll
-            for (int mat = 0; mat < NA; ++mat)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const v4i af = *reinterpret_cast<const v4i *>(
-                        &As[mat][(wn * WN + fn * 32 + (lane & 31)) * kLdsStride + col]);
-#pragma unroll
-                    for (int fm = 0; fm < FM; ++fm)
-                        acc[mat][fn][fm] =
-                            __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[fm], acc[mat][fn][fm], 0, 0, 0);
-                }
-        }
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b, acc[mat][fm][fn], 0, 0, 0);
+            }
+    };
+
+    // prologue: the tile's per-token sum_k q and s (rows past m re-read the last
+    // token), then steps 0..DB-1, all by direct loads; steps 0 and 1 landed
+    if (wave * 64 < BM) {
+        int64_t m = m0 + wave * 64 + lane;
+        m = m < a.m ? m : a.m - 1;
+        const uint32_t toff = (uint32_t)(m - m0) * 4;
+        dma4(a.sumq + m0, toff, lds0 + TQ + wave * 256);
+        if constexpr (EPI != EPI_ACC) dma4(a.s + m0, toff, lds0 + TS + wave * 256);
     }
+    for (int j = 0; j < DB; ++j)
+        if (j < nks) dma_step(j, j * X_TILE, j * W_STAGE);
+    if (DB < nks) ring_barrier<(DB - 2) * DPS>();
+    else ring_barrier<0>();
 
-    // epilogue
-    const bool vec_ok = (a.n % 4) == 0;
+    // ring positions (byte offsets): x of steps ks and ks+1, w of step ks+1, and
+    // the stages step ks+DB is loaded into
+    uint32_t xo_cur = 0, xo_nxt = X_TILE, wo_nxt = W_STAGE;
+    uint32_t xo_iss = DB * X_TILE, wo_iss = 0;
+    auto adv = [](uint32_t &o, uint32_t step, uint32_t end) {
+        o += step;
+        o = o >= end ? o - end : o;
+    };
+
+    v2u wA[NA][FN], wB[NA][FN];
+    v4i x[FM];
+    read_w(wl, wA);
+    read_x(xl0, x);
+
+    // Before the barrier that ends step ks, step ks+2 must have landed: step
+    // ks+1 reads its packed weights and its first activation half. The reads of
+    // the next step's data run unconditionally (straight-line code keeps the
+    // compiler's LDS wait counts exact); in the last step they read stages that
+    // are never used.
+    auto step = [&](int ks, v2u (&wc)[NA][FN], v2u (&wn)[NA][FN]) {
+        const bool issue = ks + DB < nks;
+        if (issue) dma_step(ks + DB, xo_iss, wo_iss);
+        v4i y[FM];
+        read_x(xl1 + xo_cur, y);
+        read_w(wl + wo_nxt, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(x, wc, std::integral_constant<int, 0>());
+        __builtin_amdgcn_sched_barrier(0);
+        read_x(xl0 + xo_nxt, x);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(y, wc, std::integral_constant<int, 1>());
+        adv(xo_cur, X_TILE, SBX * X_TILE);
+        adv(xo_nxt, X_TILE, SBX * X_TILE);
+        adv(wo_nxt, W_STAGE, SBW * W_STAGE);
+        adv(xo_iss, X_TILE, SBX * X_TILE);
+        adv(wo_iss, W_STAGE, SBW * W_STAGE);
+        if (issue) ring_barrier<VM_SLACK>();
+        else ring_barrier<0>();
+    };
+    // two steps per iteration so the packed-weight registers alternate without
+    // copies; no branch inside the body (a merge of the accumulators there costs
+    // register-class copies), the odd last step runs after the loop
+    int ks = 0;
+    for (; ks + 1 < nks; ks += 2) {
+        step(ks, wA, wB);
+        step(ks + 1, wB, wA);
+    }
+    if (ks < nks) step(ks, wA, wB);
+
+    // epilogue: y = (float)(acc - sumq) * ((s / 127) * gamma); the loop's last
+    // barrier made the per-token terms visible. Interior tiles store without
+    // bounds checks, one row pointer per token and immediate offsets per block.
+    float *const out = a.out;
+    int32_t *const acc_out = a.acc_out;
+    const int64_t M = a.m, N = a.n;
+    const int *tok_sq = reinterpret_cast<const int *>(smem + TQ);
+    const float *tok_s = reinterpret_cast<const float *>(smem + TS);
+    float g0 = 0.0f, g1 = 0.0f;
+    if constexpr (EPI != EPI_ACC) {
+        g0 = a.gamma0[0];
+        if constexpr (DUAL) g1 = a.gamma1[0];
+    }
+    auto epilogue = [&](auto full_c, auto acc_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        constexpr bool ACC = decltype(acc_c)::value;  // int32 results stored (as well)
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int64_t m = m0 + wm * WM + fm * 32 + (lane & 31);
-        if (m >= a.m) continue;
-        const int sq = a.sumq[m];
-        float c0 = 0.0f, c1 = 0.0f;  // the integer-only epilogue has no scales
-        if constexpr (EPI != EPI_ACC) {
-            const float s = a.s[m];
-            c0 = token_scale(s, a.gamma0[0]);
-            if constexpr (DUAL) c1 = token_scale(s, a.gamma1[0]);
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t n = n0 + wn * WN + fn * 32 + 8 * j + 4 * (lane >> 5);
-                int va[4];
-                float o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    va[e] = acc[0][fn][fm][4 * j + e] - sq;
-                    if constexpr (DUAL) {
-                        const int vb = acc[NA - 1][fn][fm][4 * j + e] - sq;
-                        o[e] = sq_relu_gate((float)va[e] * c0, (float)vb * c1);
-                    } else {
-                        o[e] = (float)va[e] * c0;
-                    }
-                }
-                if (vec_ok && n + 3 < a.n) {
-                    if constexpr (EPI != EPI_ACC)
-                        *reinterpret_cast<float4 *>(a.out + m * a.n + n) = make_float4(o[0], o[1], o[2], o[3]);
-                    if (EPI == EPI_ACC || (EPI == EPI_Y && a.acc_out))
-                        *reinterpret_cast<int4 *>(a.acc_out + m * a.n + n) = make_int4(va[0], va[1], va[2], va[3]);
-                } else {
+                const int r = wave * WM + fm * 32 + 8 * j + 4 * lhalf;  // tile row of register 4j
+                const v4i sq = *reinterpret_cast<const v4i *>(tok_sq + r);
+                float c0e[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (EPI != EPI_ACC) {
+                    const float4 sv = *reinterpret_cast<const float4 *>(tok_s + r);
+                    const float se[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        if (n + e < a.n) {
-                            if constexpr (EPI != EPI_ACC) a.out[m * a.n + n + e] = o[e];
-                            if (EPI == EPI_ACC || (EPI == EPI_Y && a.acc_out)) a.acc_out[m * a.n + n + e] = va[e];
+                        c0e[e] = token_scale(se[e], g0);
+                        if constexpr (DUAL) c1e[e] = token_scale(se[e], g1);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = m0 + r + e;
+                    if (!FULL && m >= M) continue;
+                    const int64_t row = m * N + n0 + lrow;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        if (!FULL && n0 + fn * 32 + lrow >= N) continue;
+                        const int va = acc[0][fm][fn][4 * j + e] - sq[e];
+                        if constexpr (EPI != EPI_ACC) {
+                            float o;
+                            if constexpr (DUAL) o = sq_relu_gate((float)va * c0e[e], (float)(acc[NA - 1][fm][fn][4 * j + e] - sq[e]) * c1e[e]);
+                            else o = (float)va * c0e[e];
+                            out[row + fn * 32] = o;
                         }
+                        if constexpr (ACC) acc_out[row + fn * 32] = va;
                     }
                 }
             }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+    if constexpr (EPI == EPI_ACC) {
+        if (full) epilogue(T(), T());
+        else epilogue(F(), T());
+    } else if constexpr (EPI == EPI_Y) {
+        if (acc_out) {
+            if (full) epilogue(T(), T());
+            else epilogue(F(), T());
+        } else {
+            if (full) epilogue(T(), F());
+            else epilogue(F(), F());
+        }
+    } else {
+        if (full) epilogue(T(), F());
+        else epilogue(F(), F());
     }
 }
 
-template <int BN, int BM, int WN, int WM>
-static void launch_tile(const GemmArgs &a, int epi, hipStream_t st)
+template <int FM, int FN, int EPI, int DB>
+static hipError_t launch_tile(GemmArgs a, hipStream_t st)
 {
-    const dim3 grid((unsigned)ceil_div(a.n, BN), (unsigned)ceil_div(a.m, BM));
-    switch (epi) {
-    case EPI_Y: hipLaunchKernelGGL((gemm_kernel<BN, BM, WN, WM, EPI_Y>), grid, dim3(kThreads), 0, st, a); break;
-    case EPI_ACC: hipLaunchKernelGGL((gemm_kernel<BN, BM, WN, WM, EPI_ACC>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<BN, BM, WN, WM, EPI_GATE>), grid, dim3(kThreads), 0, st, a); break;
+    constexpr int NA = EPI == EPI_GATE ? 2 : 1;
+    constexpr size_t lds = (size_t)(DB + 1) * 128 * FM * 64 + (size_t)DB * NA * 256 * 16 + 2 * 128 * FM * 4;
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    a.n_tiles = (int)ceil_div(a.n, 32 * FN);
+    a.m_tiles = (int)ceil_div(a.m, 128 * FM);
+    const auto kern = gemm_kernel<FM, FN, EPI, DB>;
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
+        return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_tiles * a.m_tiles)), dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+// Tile shape: the (FM, FN) whose tile count fills the 256 CUs in the fewest
+// rounds, by a per-tile cost of FM*FN*NA MFMA blocks plus a fixed per-step
+// overhead. Shapes are limited to those whose accumulators and operands fit
+// the register file without spilling: at most 14 accumulator blocks for one
+// matrix and 12 for the gate/up pair.
+struct TileShape {
+    int fm, fn;
+};
+static bool tile_allowed(int fm, int fn, int na)
+{
+    if (na == 2) return fm == 1 && fn <= 6;
+    return fm * fn <= 14;
+}
+static TileShape pick_tile(int64_t m, int64_t n, int na)
+{
+    TileShape best{1, 4};
+    double best_cost = 1e300;
+    for (int fm = 2; fm >= 1; --fm)
+        for (int fn = 8; fn >= 4; --fn) {
+            if (!tile_allowed(fm, fn, na)) continue;
+            const int64_t tiles = ceil_div(n, 32 * fn) * ceil_div(m, 128 * fm);
+            const int64_t rounds = ceil_div(tiles, 256);
+            const double cost = (double)rounds * (fm * fn * na + 3.0);
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = TileShape{fm, fn};
+            }
+        }
+    return best;
+}
+
+template <int EPI>
+static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
+{
+    constexpr int NA = EPI == EPI_GATE ? 2 : 1;
+    const TileShape t = pick_tile(a.m, a.n, NA);
+    if constexpr (NA == 1) {
+        if (t.fm == 2) {
+            switch (t.fn) {
+            case 4: return launch_tile<2, 4, EPI, 6>(a, st);
+            case 5: return launch_tile<2, 5, EPI, 6>(a, st);
+            case 6: return launch_tile<2, 6, EPI, 6>(a, st);
+            default: return launch_tile<2, 7, EPI, 6>(a, st);
+            }
+        }
+        switch (t.fn) {
+        case 4: return launch_tile<1, 4, EPI, 8>(a, st);
+        case 5: return launch_tile<1, 5, EPI, 8>(a, st);
+        case 6: return launch_tile<1, 6, EPI, 8>(a, st);
+        case 7: return launch_tile<1, 7, EPI, 8>(a, st);
+        default: return launch_tile<1, 8, EPI, 8>(a, st);
+        }
+    } else {
+        switch (t.fn) {
+        case 4: return launch_tile<1, 4, EPI, 8>(a, st);
+        case 5: return launch_tile<1, 5, EPI, 8>(a, st);
+        default: return launch_tile<1, 6, EPI, 8>(a, st);
+        }
     }
 }
 
@@ -206,13 +444,12 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t st)
     a.qp = p.qp; a.kp = p.kp; a.s = p.s; a.sumq = p.sumq; a.m = p.m; a.n = p.n;
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw; a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out;
-    if (p.m <= 32)
-        launch_tile<256, 32, 64, 32>(a, p.epi, st);
-    else if (p.m <= 64)
-        launch_tile<256, 64, 64, 64>(a, p.epi, st);
-    else
-        launch_tile<128, 128, 64, 64>(a, p.epi, st);
-    return hipGetLastError();
+    a.n_tiles = a.m_tiles = 0;
+    switch (p.epi) {
+    case EPI_Y: return launch_epi<EPI_Y>(a, st);
+    case EPI_ACC: return launch_epi<EPI_ACC>(a, st);
+    default: return launch_epi<EPI_GATE>(a, st);
+    }
 }
 
 }  // namespace bl

@@ -59,4 +59,14 @@ struct GemmProblem {
 };
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t st);
 
+// ---- 5..64 tokens: weight-streaming MFMA kernel, same problem description
+bool skinny_supported(int64_t m);
+hipError_t launch_skinny(const GemmProblem &p, hipStream_t st);
+
+// MFMA path for m tokens: the skinny kernel up to 64 tokens, the tiled GEMM above
+inline hipError_t launch_contraction(const GemmProblem &p, hipStream_t st)
+{
+    return skinny_supported(p.m) ? launch_skinny(p, st) : launch_gemm(p, st);
+}
+
 }  // namespace bl
