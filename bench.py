@@ -17,13 +17,19 @@ layers on the int8 MFMA path; TOPS = 2*M*N*K per layer / step time.
 Timing: HIP events on the stream the kernels run on. `roofline` uses the
 dominant kernel's average launch duration from per-launch event pairs.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+`--profile decode|prefill` runs the workload eagerly (no graph capture, no
+JSON line) for profilers: `--steps` steps, then one plain device copy of
+256 MiB whose HBM byte counters calibrate those of the kernels.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -38,6 +44,10 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 METRIC = "W1.58A8 BitLinear: decode GB/s vs HBM peak; prefill int8 TOPS vs MFMA peak"
+
+
+DECODE_COUNTERS = os.path.join("profiles", "gemv_decode_m1_2560x6912_6912x2560.md")
+DECODE_SOURCES = [os.path.join("bit_ternary_weight_bitlinear_amd", "csrc", f) for f in ("gemv.hip", "common.hpp")]
 
 
 def log(*a):
@@ -116,6 +126,26 @@ def rotation_pool(torch, mats, pool_bytes):
     copies = max(2, int(np.ceil(pool_bytes / per)))
     pool = [[(p.clone(), g) for p, g in mats] for _ in range(copies)]
     return pool, copies * per
+
+
+def counter_traffic():
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (each counter scaled by what it reads for a
+    plain copy of known size), or None when the kernel's sources differ from
+    the ones the counters were taken with."""
+    try:
+        with open(os.path.join(ROOT, DECODE_COUNTERS)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^(traffic_bytes_per_launch|source-sha256): (\S+)$", text, re.M))
+    h = hashlib.sha256()
+    for src in DECODE_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("source-sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 # --------------------------------------------------------------------------- workloads
@@ -230,6 +260,38 @@ def bench_ffn(bl, torch, dev, steps, warmup):
     return out
 
 
+def profile_run(bl, torch, dev, what, steps, pool_mb):
+    """Eager launches of one workload for rocprofv3, then a 256 MiB copy."""
+    if what == "decode":
+        cfg = synth.WORKLOADS[2]
+        mats, xs, ys = [], [], []
+        for tid, (k, n) in zip(("up", "down"), cfg["mats"]):
+            mats.append(make_weights(bl, torch, 2, tid, n, k, dev))
+            xs.append(act_tensor(torch, 2, 1, k, dev, outlier_channels=round(0.01 * k),
+                                 outlier_scale=cfg["outlier_scale"]))
+            ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        for i in range(steps):
+            ws = pool[i % len(pool)]
+            for j in range(2):
+                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
+    else:
+        cfg = synth.WORKLOADS[4]
+        m = cfg["m"]
+        for tid, (k, n) in zip(("up", "down"), cfg["mats"]):
+            packed, gamma = make_weights(bl, torch, 4, tid, n, k, dev)
+            x = act_tensor(torch, 4, m, k, dev, heavy_channels=round(0.01 * k))
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            ws = torch.empty(bl.workspace_size(bl.OP_FORWARD, m, k, n), dtype=torch.uint8, device=dev)
+            for i in range(steps):
+                bl.forward(x, packed, gamma, out=y, workspace=ws)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profile {what}: {steps} steps, then one 256 MiB copy")
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -268,6 +330,8 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--workload", choices=["default", "all"], default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill"], default=None,
+                    help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -280,6 +344,9 @@ def main():
     bl.load_library()
     dev = torch.device("cuda:0")
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.profile:
+        profile_run(bl, torch, dev, args.profile, args.steps, args.pool_mb)
+        return
 
     dec, _ = bench_decode(bl, torch, dev, args.steps, args.warmup, args.pool_mb)
     log(f"decode: {dec['ms_per_step']*1e3:.2f} us/step, {dec['gbs']:.1f} GB/s packed, "
@@ -294,8 +361,11 @@ def main():
         log("ffn:", json.dumps(extra["ffn_8b"]))
 
     achieved = dec["algo_bytes_per_launch"] / dec["kernel_mean_s"] / 1e9
+    traffic = counter_traffic()
     roofline = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    traffic_note=(f"HBM bytes per launch, {DECODE_COUNTERS}" if traffic else
+                                  "no counter summary for the current decode kernel sources"),
                     kernel="gemv_kernel (decode, fused act-quant + v_dot4)",
                     algo_bytes_per_launch=dec["algo_bytes_per_launch"],
                     mean_launch_us=round(dec["kernel_mean_s"] * 1e6, 3),
