@@ -115,10 +115,93 @@ __device__ inline void ring_barrier()
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-__device__ inline v4i expand_b(uint32_t w)
+// one v_lshrrev_b64 (written out: the compiler would split a 64-bit shift whose
+// high bits are masked off into two 32-bit shifts)
+template <int S>
+__device__ inline uint64_t shr64(uint64_t v)
 {
-    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-               (int)((w >> 6) & 0x03030303u)};
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(v));
+    return r;
+}
+
+// Epilogue of one wave: y = (float)(acc - sumq) * ((s / 127) * gamma) for its
+// 32*FM tokens (tile rows wave*32*FM ..) x 32*FN features. tok_sq / tok_s hold
+// sum_k q and s of the tile's tokens (LDS). Interior tiles store without bounds
+// checks, one row pointer per token and immediate offsets per block.
+template <int FM, int FN, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[EPI == EPI_GATE ? 2 : 1][FM][FN],
+                                           const int *tok_sq, const float *tok_s, int64_t m0, int64_t n0,
+                                           int wave, int lrow, int lhalf)
+{
+    constexpr bool DUAL = EPI == EPI_GATE;
+    constexpr int NA = DUAL ? 2 : 1;
+    constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
+    float *const out = a.out;
+    int32_t *const acc_out = a.acc_out;
+    const int64_t M = a.m, N = a.n;
+    float g0 = 0.0f, g1 = 0.0f;
+    if constexpr (EPI != EPI_ACC) {
+        g0 = a.gamma0[0];
+        if constexpr (DUAL) g1 = a.gamma1[0];
+    }
+    auto epilogue = [&](auto full_c, auto acc_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        constexpr bool ACC = decltype(acc_c)::value;  // int32 results stored (as well)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = wave * WM + fm * 32 + 8 * j + 4 * lhalf;  // tile row of register 4j
+                const v4i sq = *reinterpret_cast<const v4i *>(tok_sq + r);
+                float c0e[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (EPI != EPI_ACC) {
+                    const float4 sv = *reinterpret_cast<const float4 *>(tok_s + r);
+                    const float se[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        c0e[e] = token_scale(se[e], g0);
+                        if constexpr (DUAL) c1e[e] = token_scale(se[e], g1);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = m0 + r + e;
+                    if (!FULL && m >= M) continue;
+                    const int64_t row = m * N + n0 + lrow;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        if (!FULL && n0 + fn * 32 + lrow >= N) continue;
+                        const int va = acc[0][fm][fn][4 * j + e] - sq[e];
+                        if constexpr (EPI != EPI_ACC) {
+                            float o;
+                            if constexpr (DUAL) o = sq_relu_gate((float)va * c0e[e], (float)(acc[NA - 1][fm][fn][4 * j + e] - sq[e]) * c1e[e]);
+                            else o = (float)va * c0e[e];
+                            out[row + fn * 32] = o;
+                        }
+                        if constexpr (ACC) acc_out[row + fn * 32] = va;
+                    }
+                }
+            }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+    if constexpr (EPI == EPI_ACC) {
+        if (full) epilogue(T(), T());
+        else epilogue(F(), T());
+    } else if constexpr (EPI == EPI_Y) {
+        if (acc_out) {
+            if (full) epilogue(T(), T());
+            else epilogue(F(), T());
+        } else {
+            if (full) epilogue(T(), F());
+            else epilogue(F(), F());
+        }
+    } else {
+        if (full) epilogue(T(), F());
+        else epilogue(F(), F());
+    }
 }
 
 template <int FM, int FN, int EPI, int DB>
@@ -213,17 +296,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mat][fm][fn][v] = 0;
 
-    auto mfma_half = [&](const v4i (&x)[FM], const v2u (&w)[NA][FN], auto hc) {
-        constexpr int h = decltype(hc)::value;
+    // Operands of both half steps from one packed fragment: with the two dwords
+    // as one 64-bit value, one shift gives field i of both (the bits a shift
+    // moves across the dword boundary fall outside the 0x03030303 mask).
+    auto expand2 = [](v2u w, v4i &b0, v4i &b1) {
+        constexpr uint32_t M = 0x03030303u;
+        const uint64_t v = ((uint64_t)w.y << 32) | w.x;
+        const uint64_t v2 = shr64<2>(v), v4 = shr64<4>(v), v6 = shr64<6>(v);
+        b0 = v4i{(int)(w.x & M), (int)((uint32_t)v2 & M), (int)((uint32_t)v4 & M), (int)((uint32_t)v6 & M)};
+        b1 = v4i{(int)(w.y & M), (int)((uint32_t)(v2 >> 32) & M), (int)((uint32_t)(v4 >> 32) & M),
+                 (int)((uint32_t)(v6 >> 32) & M)};
+    };
+    // first half step: expands every fragment but the first (whose operands
+    // were prepared before the barrier), keeping the second half's operands,
+    // and runs the MFMAs of the first half as soon as each is ready
+    auto mfma_half0_rest = [&](const v4i (&x)[FM], const v2u (&w)[NA][FN], v4i (&b1)[NA][FN]) {
 #pragma unroll
         for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const v4i b = expand_b(w[mat][fn][h]);
+                if (mat == 0 && fn == 0) continue;
+                v4i b0;
+                expand2(w[mat][fn], b0, b1[mat][fn]);
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
-                    acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b, acc[mat][fm][fn], 0, 0, 0);
+                    acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b0, acc[mat][fm][fn], 0, 0, 0);
             }
+    };
+    auto mfma_half1 = [&](const v4i (&x)[FM], const v4i (&b1)[NA][FN]) {
+#pragma unroll
+        for (int mat = 0; mat < NA; ++mat)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b1[mat][fn], acc[mat][fm][fn], 0, 0, 0);
     };
 
     // prologue: the tile's per-token sum_k q and s (rows past m re-read the last
@@ -253,29 +360,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     v4i x[FM];
     read_w(wl, wA);
     read_x(xl0, x);
+    v4i p0, p1;  // both half-step operands of fragment (0, 0) of the coming step
+    expand2(wA[0][0], p0, p1);
 
     // Before the barrier that ends step ks, step ks+2 must have landed: step
     // ks+1 reads its packed weights and its first activation half. The reads of
     // the next step's data run unconditionally (straight-line code keeps the
     // compiler's LDS wait counts exact); in the last step they read stages that
-    // are never used.
+    // are never used. Right after the barrier the first MFMAs start on operands
+    // already in registers; the direct loads, the reads of this step's second
+    // activation half and of the next step's packed weights go out in their
+    // shadow, and the ring advance and the next step's first expansion run
+    // between the second half's MFMAs.
     auto step = [&](int ks, v2u (&wc)[NA][FN], v2u (&wn)[NA][FN]) {
         const bool issue = ks + DB < nks;
+        v4i b1[NA][FN];
+        b1[0][0] = p1;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            acc[0][fm][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], p0, acc[0][fm][0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         if (issue) dma_step(ks + DB, xo_iss, wo_iss);
         v4i y[FM];
         read_x(xl1 + xo_cur, y);
         read_w(wl + wo_nxt, wn);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(x, wc, std::integral_constant<int, 0>());
+        mfma_half0_rest(x, wc, b1);
         __builtin_amdgcn_sched_barrier(0);
         read_x(xl0 + xo_nxt, x);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_half(y, wc, std::integral_constant<int, 1>());
+        mfma_half1(y, b1);
         adv(xo_cur, X_TILE, SBX * X_TILE);
         adv(xo_nxt, X_TILE, SBX * X_TILE);
         adv(wo_nxt, W_STAGE, SBW * W_STAGE);
         adv(xo_iss, X_TILE, SBX * X_TILE);
         adv(wo_iss, W_STAGE, SBW * W_STAGE);
+        expand2(wn[0][0], p0, p1);
         if (issue) ring_barrier<VM_SLACK>();
         else ring_barrier<0>();
     };
@@ -289,76 +409,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
     if (ks < nks) step(ks, wA, wB);
 
-    // epilogue: y = (float)(acc - sumq) * ((s / 127) * gamma); the loop's last
-    // barrier made the per-token terms visible. Interior tiles store without
-    // bounds checks, one row pointer per token and immediate offsets per block.
-    float *const out = a.out;
-    int32_t *const acc_out = a.acc_out;
-    const int64_t M = a.m, N = a.n;
-    const int *tok_sq = reinterpret_cast<const int *>(smem + TQ);
-    const float *tok_s = reinterpret_cast<const float *>(smem + TS);
-    float g0 = 0.0f, g1 = 0.0f;
-    if constexpr (EPI != EPI_ACC) {
-        g0 = a.gamma0[0];
-        if constexpr (DUAL) g1 = a.gamma1[0];
-    }
-    auto epilogue = [&](auto full_c, auto acc_c) {
-        constexpr bool FULL = decltype(full_c)::value;
-        constexpr bool ACC = decltype(acc_c)::value;  // int32 results stored (as well)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wave * WM + fm * 32 + 8 * j + 4 * lhalf;  // tile row of register 4j
-                const v4i sq = *reinterpret_cast<const v4i *>(tok_sq + r);
-                float c0e[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (EPI != EPI_ACC) {
-                    const float4 sv = *reinterpret_cast<const float4 *>(tok_s + r);
-                    const float se[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        c0e[e] = token_scale(se[e], g0);
-                        if constexpr (DUAL) c1e[e] = token_scale(se[e], g1);
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t m = m0 + r + e;
-                    if (!FULL && m >= M) continue;
-                    const int64_t row = m * N + n0 + lrow;
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        if (!FULL && n0 + fn * 32 + lrow >= N) continue;
-                        const int va = acc[0][fm][fn][4 * j + e] - sq[e];
-                        if constexpr (EPI != EPI_ACC) {
-                            float o;
-                            if constexpr (DUAL) o = sq_relu_gate((float)va * c0e[e], (float)(acc[NA - 1][fm][fn][4 * j + e] - sq[e]) * c1e[e]);
-                            else o = (float)va * c0e[e];
-                            out[row + fn * 32] = o;
-                        }
-                        if constexpr (ACC) acc_out[row + fn * 32] = va;
-                    }
-                }
-            }
-    };
-    using T = std::true_type;
-    using F = std::false_type;
-    const bool full = m0 + BM <= M && n0 + BN <= N;
-    if constexpr (EPI == EPI_ACC) {
-        if (full) epilogue(T(), T());
-        else epilogue(F(), T());
-    } else if constexpr (EPI == EPI_Y) {
-        if (acc_out) {
-            if (full) epilogue(T(), T());
-            else epilogue(F(), T());
-        } else {
-            if (full) epilogue(T(), F());
-            else epilogue(F(), F());
-        }
-    } else {
-        if (full) epilogue(T(), F());
-        else epilogue(F(), F());
-    }
+    // epilogue (the loop's last barrier made the per-token terms visible)
+    store_tile<FM, FN, EPI>(a, acc, reinterpret_cast<const int *>(smem + TQ), reinterpret_cast<const float *>(smem + TS),
+                            m0, n0, wave, lrow, lhalf);
 }
 
 template <int FM, int FN, int EPI, int DB>
