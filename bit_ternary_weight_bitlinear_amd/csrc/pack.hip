@@ -13,38 +13,64 @@
 
 namespace bl {
 
-// One wave per 64 rows. 64x64 tiles of W are staged through LDS so that the
-// global reads are coalesced while each lane walks its own row in k order.
+// One thread per row: each row is one sequential fp64 chain (the order the
+// definition fixes), so the parallelism is across rows. A lane keeps two
+// batches of its row in flight (16 independent 16-byte loads each) and adds
+// the current one in column order while the next arrives; a wave's 64 rows
+// share each cache line over four consecutive loads.
 __global__ __launch_bounds__(64) void absmean_rowsum_kernel(const float *__restrict__ w, int64_t n,
                                                             int64_t k, double *__restrict__ rowsum)
 {
-    __shared__ float tile[64][65];
-    const int lane = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    constexpr int B = 16;  // float4 loads per batch (64 weights)
+    const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (r >= n) return;
+    const float *row = w + r * k;
+    const int64_t nb = k / (4 * B);
     double acc = 0.0;
-    for (int64_t c0 = 0; c0 < k; c0 += 64) {
-        const int64_t c = c0 + lane;
-#pragma unroll 8
-        for (int i = 0; i < 64; ++i) {
-            const int64_t r = r0 + i;
-            tile[i][lane] = (r < n && c < k) ? w[r * k + c] : 0.0f;
+    auto add = [&](const float4 (&v)[B]) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            acc += fabs((double)v[i].x);
+            acc += fabs((double)v[i].y);
+            acc += fabs((double)v[i].z);
+            acc += fabs((double)v[i].w);
         }
-        __syncthreads();
-        const int cnt = (int)((k - c0) < 64 ? (k - c0) : 64);
-        for (int j = 0; j < cnt; ++j) acc += fabs((double)tile[lane][j]);
-        __syncthreads();
+    };
+    float4 cur[B], nxt[B];
+    if (nb > 0) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) cur[i] = *reinterpret_cast<const float4 *>(row + 4 * i);
     }
-    if (r0 + lane < n) rowsum[r0 + lane] = acc;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t bn = b + 1 < nb ? b + 1 : b;  // the last batch re-reads itself (unused)
+#pragma unroll
+        for (int i = 0; i < B; ++i) nxt[i] = *reinterpret_cast<const float4 *>(row + bn * 4 * B + 4 * i);
+        add(cur);
+#pragma unroll
+        for (int i = 0; i < B; ++i) cur[i] = nxt[i];
+    }
+    for (int64_t c = nb * 4 * B; c < k; ++c) acc += fabs((double)row[c]);
+    rowsum[r] = acc;
 }
 
-// Sequential sum of the row sums (row order), one division, one rounding to fp32.
-__global__ void absmean_finish_kernel(const double *__restrict__ rowsum, int64_t n, int64_t k,
-                                      float *__restrict__ gamma)
+// Sequential sum of the row sums (row order), one division, one rounding to
+// fp32. The workgroup stages the row sums in LDS with coalesced loads; thread 0
+// adds them in order.
+__global__ __launch_bounds__(256) void absmean_finish_kernel(const double *__restrict__ rowsum, int64_t n,
+                                                             int64_t k, float *__restrict__ gamma)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    constexpr int CH = 2048;
+    __shared__ double buf[CH];
     double total = 0.0;
-    for (int64_t r = 0; r < n; ++r) total += rowsum[r];
-    gamma[0] = (float)(total / ((double)n * (double)k));
+    for (int64_t base = 0; base < n; base += CH) {
+        const int cnt = (int)((n - base) < CH ? (n - base) : CH);
+        for (int i = threadIdx.x; i < cnt; i += blockDim.x) buf[i] = rowsum[base + i];
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int i = 0; i < cnt; ++i) total += buf[i];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) gamma[0] = (float)(total / ((double)n * (double)k));
 }
 
 // One packed byte per thread (four weights, one 16-byte load).
@@ -77,7 +103,7 @@ hipError_t launch_pack(const float *w, int64_t n, int64_t k, uint8_t *packed, fl
 {
     hipLaunchKernelGGL(absmean_rowsum_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(64), 0, st, w, n,
                        k, rowsum);
-    hipLaunchKernelGGL(absmean_finish_kernel, dim3(1), dim3(64), 0, st, rowsum, n, k, gamma);
+    hipLaunchKernelGGL(absmean_finish_kernel, dim3(1), dim3(256), 0, st, rowsum, n, k, gamma);
     const int64_t total = n * (k / 4);
     int64_t blocks = ceil_div(total, 256);
     if (blocks > 16384) blocks = 16384;
