@@ -8,7 +8,9 @@
 //
 // One 256-thread workgroup per token. A thread owns 16-input groups; up to four
 // groups per thread stay in registers between the absmax pass and the
-// quantization pass (k <= 16384), longer rows are read twice. The absmax and
+// quantization pass (k <= 16384), longer rows are read twice. The number of
+// resident groups is a template parameter sized to the row at launch, so short
+// rows keep few registers and many tokens are in flight per CU. The absmax and
 // the sum of the codes are reduced with DPP inside each wave and through LDS
 // across the four waves. HBM-bound: it reads the row once and writes k bytes.
 #include "common.hpp"
@@ -48,7 +50,7 @@ __device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const uint4 
 
 constexpr int kResidentGroups = 4;
 
-template <typename T, bool FULL>
+template <typename T, bool FULL, int RG>
 __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x, int64_t k, int64_t kp,
                                                         int8_t *__restrict__ q_nat,
                                                         int8_t *__restrict__ q_perm,
@@ -59,13 +61,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     const int64_t t = blockIdx.x;
     const T *row = x + t * k;
     const int64_t G = ceil_div(k, 16);
-    const bool resident = G <= (int64_t)kResidentGroups * kThreads;
+    const bool resident = G <= (int64_t)RG * kThreads;
 
-    float v[kResidentGroups][16];
+    float v[RG][16];
     float amax = 0.0f;
     if (resident) {
 #pragma unroll
-        for (int r = 0; r < kResidentGroups; ++r) {
+        for (int r = 0; r < RG; ++r) {
             const int64_t g = threadIdx.x + r * kThreads;
             if (g < G) {
                 load_group<T, FULL>(row, k, g, v[r]);
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     };
     if (resident) {
 #pragma unroll
-        for (int r = 0; r < kResidentGroups; ++r) {
+        for (int r = 0; r < RG; ++r) {
             const int64_t g = threadIdx.x + r * kThreads;
             if (g < G) emit(g, v[r]);
         }
@@ -114,27 +116,34 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     if (threadIdx.x == 0) s[t] = st;
 }
 
+template <typename T, bool FULL>
+static void launch_rg(const T *x, int64_t m, int64_t k, int64_t kp, int8_t *q_nat, int8_t *q_perm, float *s,
+                      int32_t *sumq, hipStream_t st)
+{
+    const dim3 grid((unsigned)m), block(kThreads);
+    const int64_t groups = ceil_div(k, 16);
+    const int64_t rg = ceil_div(groups, kThreads);
+    if (rg <= 1)
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 1>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s, sumq);
+    else if (rg == 2)
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 2>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s, sumq);
+    else
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, kResidentGroups>), grid, block, 0, st, x, k, kp, q_nat,
+                           q_perm, s, sumq);
+}
+
 hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, int8_t *q_nat,
                             int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
 {
-    const dim3 grid((unsigned)m), block(kThreads);
     const bool full = k % 16 == 0;
     if (bf16) {
         const bf16_t *xb = static_cast<const bf16_t *>(x);
-        if (full)
-            hipLaunchKernelGGL((act_quant_kernel<bf16_t, true>), grid, block, 0, st, xb, k, kp, q_nat,
-                               q_perm, s, sumq);
-        else
-            hipLaunchKernelGGL((act_quant_kernel<bf16_t, false>), grid, block, 0, st, xb, k, kp, q_nat,
-                               q_perm, s, sumq);
+        if (full) launch_rg<bf16_t, true>(xb, m, k, kp, q_nat, q_perm, s, sumq, st);
+        else launch_rg<bf16_t, false>(xb, m, k, kp, q_nat, q_perm, s, sumq, st);
     } else {
         const float *xf = static_cast<const float *>(x);
-        if (full)
-            hipLaunchKernelGGL((act_quant_kernel<float, true>), grid, block, 0, st, xf, k, kp, q_nat,
-                               q_perm, s, sumq);
-        else
-            hipLaunchKernelGGL((act_quant_kernel<float, false>), grid, block, 0, st, xf, k, kp, q_nat,
-                               q_perm, s, sumq);
+        if (full) launch_rg<float, true>(xf, m, k, kp, q_nat, q_perm, s, sumq, st);
+        else launch_rg<float, false>(xf, m, k, kp, q_nat, q_perm, s, sumq, st);
     }
     return hipGetLastError();
 }
