@@ -204,7 +204,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
     }
 }
 
-template <int FM, int FN, int EPI, int DB>
+// SPB: 64-input steps per ring stage (1 or 2). With 2, the direct loads of a
+// stage go out once per pair of steps and the barrier runs once per pair; the
+// step count must be even. DB: stages requested ahead.
+template <int FM, int FN, int EPI, int DB, int SPB>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
     constexpr bool DUAL = EPI == EPI_GATE;
@@ -212,18 +215,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
     static_assert(FM * FN * NA <= 16, "accumulators fit the 256 AGPRs");
     static_assert(BN <= 256, "packed rows: one 64-row direct load per wave");
-    static_assert(DB >= 3, "at least one step of slack for the direct loads");
-    constexpr int SBX = DB + 1;            // activation stages (steps ks .. ks+DB live)
-    constexpr int SBW = DB;                // packed-weight stages (steps ks+1 .. ks+DB live)
+    static_assert(DB >= 3, "at least one stage of slack for the direct loads");
+    static_assert(SPB == 1 || SPB == 2, "one or two steps per stage");
     constexpr int X_TILE = BM * 64;        // activation bytes per step
     constexpr int W_PK = 256 * 16;         // packed bytes per step and matrix (256 rows)
-    constexpr int W_STAGE = NA * W_PK;
+    constexpr int W_STAGE = NA * W_PK;     // packed bytes per step
+    constexpr int XS = SPB * X_TILE, WS = SPB * W_STAGE;  // bytes per ring stage
+    // Live stages: activations of stages S .. S+DB; packed weights of S+1 .. S+DB,
+    // and with two steps per stage also S (its second step's weights are read
+    // during its first step).
+    constexpr int SBX = DB + 1;
+    constexpr int SBW = SPB == 1 ? DB : DB + 1;
     constexpr int X_INSTR = BM / 64;       // activation direct loads per thread per step
-    constexpr int DPS = X_INSTR + NA;      // direct loads per thread per step
+    constexpr int DPS = SPB * (X_INSTR + NA);  // direct loads per thread per stage
     constexpr int VM_SLACK = (DB - 2) * DPS;
     static_assert(VM_SLACK < 64, "vmcnt field");
-    // LDS: xring[SBX][X_TILE], wring[SBW][NA][W_PK], then sum_k q and s of the tile's tokens
-    constexpr int XR = 0, WR = SBX * X_TILE, TQ = WR + SBW * W_STAGE, TS = TQ + BM * 4;
+    // LDS: xring[SBX][XS], wring[SBW][WS], then sum_k q and s of the tile's tokens
+    constexpr int XR = 0, WR = SBX * XS, TQ = WR + SBW * WS, TS = TQ + BM * 4;
     extern __shared__ __align__(16) int8_t smem[];
     const uint32_t lds0 = lds_addr(smem);
 
@@ -258,14 +266,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         n = n < a.n ? n : a.n - 1;
         woff = (uint32_t)((n - n0) * a.ldw);
     }
-    // requests step j into the stages at byte offsets xo / wo of the rings
-    auto dma_step = [&](int j, uint32_t xo, uint32_t wo) {
+    // requests stage j (steps SPB*j ..) into the ring stages at byte offsets xo / wo
+    auto dma_stage = [&](int j, uint32_t xo, uint32_t wo) {
 #pragma unroll
-        for (int i = 0; i < X_INSTR; ++i)
-            dma16(xbase + (int64_t)j * 64, xoff[i], lds0 + XR + xo + (i * 4 + wave) * 1024);
+        for (int sub = 0; sub < SPB; ++sub) {
+            const int64_t ks = (int64_t)SPB * j + sub;
 #pragma unroll
-        for (int mat = 0; mat < NA; ++mat)
-            dma16(wbase[mat] + (int64_t)j * 16, woff, lds0 + WR + wo + mat * W_PK + wave * 1024);
+            for (int i = 0; i < X_INSTR; ++i)
+                dma16(xbase + ks * 64, xoff[i], lds0 + XR + xo + sub * X_TILE + (i * 4 + wave) * 1024);
+#pragma unroll
+            for (int mat = 0; mat < NA; ++mat)
+                dma16(wbase[mat] + ks * 16, woff, lds0 + WR + wo + sub * W_STAGE + mat * W_PK + wave * 1024);
+        }
     };
 
     // LDS read addresses: per-lane bases, stage offsets added per step
@@ -334,7 +346,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     };
 
     // prologue: the tile's per-token sum_k q and s (rows past m re-read the last
-    // token), then steps 0..DB-1, all by direct loads; steps 0 and 1 landed
+    // token), then stages 0..DB-1, all by direct loads; stages 0 and 1 landed
     if (wave * 64 < BM) {
         int64_t m = m0 + wave * 64 + lane;
         m = m < a.m ? m : a.m - 1;
@@ -342,15 +354,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         dma4(a.sumq + m0, toff, lds0 + TQ + wave * 256);
         if constexpr (EPI != EPI_ACC) dma4(a.s + m0, toff, lds0 + TS + wave * 256);
     }
+    const int nst = nks / SPB;  // stages (SPB = 2 only for an even step count)
     for (int j = 0; j < DB; ++j)
-        if (j < nks) dma_step(j, j * X_TILE, j * W_STAGE);
-    if (DB < nks) ring_barrier<(DB - 2) * DPS>();
+        if (j < nst) dma_stage(j, j * XS, j * WS);
+    if (DB < nst) ring_barrier<(DB - 2) * DPS>();
     else ring_barrier<0>();
 
-    // ring positions (byte offsets): x of steps ks and ks+1, w of step ks+1, and
-    // the stages step ks+DB is loaded into
-    uint32_t xo_cur = 0, xo_nxt = X_TILE, wo_nxt = W_STAGE;
-    uint32_t xo_iss = DB * X_TILE, wo_iss = 0;
     auto adv = [](uint32_t &o, uint32_t step, uint32_t end) {
         o += step;
         o = o >= end ? o - end : o;
@@ -363,71 +372,112 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     v4i p0, p1;  // both half-step operands of fragment (0, 0) of the coming step
     expand2(wA[0][0], p0, p1);
 
-    // Before the barrier that ends step ks, step ks+2 must have landed: step
-    // ks+1 reads its packed weights and its first activation half. The reads of
-    // the next step's data run unconditionally (straight-line code keeps the
-    // compiler's LDS wait counts exact); in the last step they read stages that
-    // are never used. Right after the barrier the first MFMAs start on operands
-    // already in registers; the direct loads, the reads of this step's second
-    // activation half and of the next step's packed weights go out in their
-    // shadow, and the ring advance and the next step's first expansion run
-    // between the second half's MFMAs.
-    auto step = [&](int ks, v2u (&wc)[NA][FN], v2u (&wn)[NA][FN]) {
-        const bool issue = ks + DB < nks;
+    // One 64-input step. Right after a barrier its first MFMAs start on
+    // operands already in registers; the direct loads (issue), the reads of this
+    // step's second activation half (ya) and of the next step's packed weights
+    // (wa) go out in their shadow, the next step's first activation half (xa)
+    // is read during the second half, and the next step's first expansion runs
+    // last. The reads of the next step's data run unconditionally (straight-line
+    // code keeps the compiler's LDS wait counts exact); in the last step they
+    // read stages that are never used.
+    auto step = [&](v2u (&wc)[NA][FN], v2u (&wn)[NA][FN], uint32_t ya, uint32_t wa, uint32_t xa, auto &&issue) {
         v4i b1[NA][FN];
         b1[0][0] = p1;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             acc[0][fm][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], p0, acc[0][fm][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (issue) dma_step(ks + DB, xo_iss, wo_iss);
+        issue();
         v4i y[FM];
-        read_x(xl1 + xo_cur, y);
-        read_w(wl + wo_nxt, wn);
+        read_x(ya, y);
+        read_w(wa, wn);
         __builtin_amdgcn_sched_barrier(0);
         mfma_half0_rest(x, wc, b1);
         __builtin_amdgcn_sched_barrier(0);
-        read_x(xl0 + xo_nxt, x);
+        read_x(xa, x);
         __builtin_amdgcn_sched_barrier(0);
         mfma_half1(y, b1);
-        adv(xo_cur, X_TILE, SBX * X_TILE);
-        adv(xo_nxt, X_TILE, SBX * X_TILE);
-        adv(wo_nxt, W_STAGE, SBW * W_STAGE);
-        adv(xo_iss, X_TILE, SBX * X_TILE);
-        adv(wo_iss, W_STAGE, SBW * W_STAGE);
         expand2(wn[0][0], p0, p1);
-        if (issue) ring_barrier<VM_SLACK>();
-        else ring_barrier<0>();
     };
-    // two steps per iteration so the packed-weight registers alternate without
-    // copies; no branch inside the body (a merge of the accumulators there costs
-    // register-class copies), the odd last step runs after the loop
-    int ks = 0;
-    for (; ks + 1 < nks; ks += 2) {
-        step(ks, wA, wB);
-        step(ks + 1, wB, wA);
+
+    // ring positions (byte offsets): the current and next stage of each ring and
+    // the stages stage S+DB is loaded into
+    uint32_t xs_cur = 0, xs_nxt = XS, ws_cur = 0, ws_nxt = WS;
+    uint32_t xs_iss = (DB % SBX) * XS, ws_iss = (DB % SBW) * WS;
+    auto advance = [&] {
+        adv(xs_cur, XS, SBX * XS);
+        adv(xs_nxt, XS, SBX * XS);
+        adv(ws_cur, WS, SBW * WS);
+        adv(ws_nxt, WS, SBW * WS);
+        adv(xs_iss, XS, SBX * XS);
+        adv(ws_iss, WS, SBW * WS);
+    };
+    // Before the barrier that ends stage S, stage S+2 must have landed: the
+    // following stage reads (part of) it before its own barrier.
+    if constexpr (SPB == 1) {
+        // one barrier per step; two steps per iteration so the packed-weight
+        // registers alternate without copies; no branch inside the body (a merge
+        // of the accumulators there costs register-class copies), the odd last
+        // step runs after the loop
+        auto one = [&](int ks, v2u (&wc)[NA][FN], v2u (&wn)[NA][FN]) {
+            const bool issue = ks + DB < nks;
+            step(wc, wn, xl1 + xs_cur, wl + ws_nxt, xl0 + xs_nxt, [&] {
+                if (issue) dma_stage(ks + DB, xs_iss, ws_iss);
+            });
+            advance();
+            if (issue) ring_barrier<VM_SLACK>();
+            else ring_barrier<0>();
+        };
+        int ks = 0;
+        for (; ks + 1 < nks; ks += 2) {
+            one(ks, wA, wB);
+            one(ks + 1, wB, wA);
+        }
+        if (ks < nks) one(ks, wA, wB);
+    } else {
+        // one barrier per pair of steps: the first step reads the second's
+        // weights and first activation half from the same stage, the second
+        // reads the next stage
+        for (int S = 0; S < nst; ++S) {
+            const bool issue = S + DB < nst;
+            step(wA, wB, xl1 + xs_cur, wl + ws_cur + W_STAGE, xl0 + xs_cur + X_TILE, [&] {
+                if (issue) dma_stage(S + DB, xs_iss, ws_iss);
+            });
+            step(wB, wA, xl1 + xs_cur + X_TILE, wl + ws_nxt, xl0 + xs_nxt, [] {});
+            advance();
+            if (issue) ring_barrier<VM_SLACK>();
+            else ring_barrier<0>();
+        }
     }
-    if (ks < nks) step(ks, wA, wB);
 
     // epilogue (the loop's last barrier made the per-token terms visible)
     store_tile<FM, FN, EPI>(a, acc, reinterpret_cast<const int *>(smem + TQ), reinterpret_cast<const float *>(smem + TS),
                             m0, n0, wave, lrow, lhalf);
 }
 
-template <int FM, int FN, int EPI, int DB>
+template <int FM, int FN, int EPI, int DB, int SPB = 1>
 static hipError_t launch_tile(GemmArgs a, hipStream_t st)
 {
     constexpr int NA = EPI == EPI_GATE ? 2 : 1;
-    constexpr size_t lds = (size_t)(DB + 1) * 128 * FM * 64 + (size_t)DB * NA * 256 * 16 + 2 * 128 * FM * 4;
+    constexpr size_t xs = (size_t)SPB * 128 * FM * 64, ws = (size_t)SPB * NA * 256 * 16;
+    constexpr size_t lds = (size_t)(DB + 1) * xs + (size_t)(SPB == 1 ? DB : DB + 1) * ws + 2 * 128 * FM * 4;
     static_assert(lds <= 160 * 1024, "LDS budget");
     a.n_tiles = (int)ceil_div(a.n, 32 * FN);
     a.m_tiles = (int)ceil_div(a.m, 128 * FM);
-    const auto kern = gemm_kernel<FM, FN, EPI, DB>;
+    const auto kern = gemm_kernel<FM, FN, EPI, DB, SPB>;
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
         return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_tiles * a.m_tiles)), dim3(kThreads), lds, st, a);
     return hipGetLastError();
+}
+
+// 128-token tiles of one matrix: two steps per stage when the step count is even
+template <int FN, int EPI>
+static hipError_t launch_fm1(const GemmArgs &a, hipStream_t st)
+{
+    if ((a.kp / 64) % 2 == 0) return launch_tile<1, FN, EPI, 5, 2>(a, st);
+    return launch_tile<1, FN, EPI, 8, 1>(a, st);
 }
 
 // Tile shape: the (FM, FN) whose tile count fills the 256 CUs in the fewest
@@ -476,11 +526,11 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
             }
         }
         switch (t.fn) {
-        case 4: return launch_tile<1, 4, EPI, 8>(a, st);
-        case 5: return launch_tile<1, 5, EPI, 8>(a, st);
-        case 6: return launch_tile<1, 6, EPI, 8>(a, st);
-        case 7: return launch_tile<1, 7, EPI, 8>(a, st);
-        default: return launch_tile<1, 8, EPI, 8>(a, st);
+        case 4: return launch_fm1<4, EPI>(a, st);
+        case 5: return launch_fm1<5, EPI>(a, st);
+        case 6: return launch_fm1<6, EPI>(a, st);
+        case 7: return launch_fm1<7, EPI>(a, st);
+        default: return launch_fm1<8, EPI>(a, st);
         }
     } else {
         switch (t.fn) {

@@ -6,7 +6,8 @@ shape the host can pick, these tests use the smallest token and feature counts
 (neither a multiple of the tile) that select it, with k = 704 or 644 inputs:
 eleven 64-input steps, more than the direct-load ring depth, so the ring runs
 in its steady state and ends on an odd step; 644 also takes the padded-weight
-path (k not a multiple of 64). Checked: int32 accumulators bit-exact, fp32
+path (k not a multiple of 64). With an even step count (k = 1536) the
+128-token tiles load and synchronize once per pair of steps. Checked: int32 accumulators bit-exact, fp32
 outputs within 1e-5 relative, FFN requantized h bit-exact.
 """
 import math
@@ -70,10 +71,13 @@ def bl():
     return m
 
 
-@pytest.mark.parametrize("fm,fn", SINGLE)
-def test_gemm_tile_shapes(bl, fm, fn):
+CASES = [(fm, fn, 704 if fm == 2 else 644) for fm, fn in SINGLE] + [(1, fn, 1536) for fm, fn in SINGLE if fm == 1]
+
+
+@pytest.mark.parametrize("fm,fn,k", CASES)
+def test_gemm_tile_shapes(bl, fm, fn, k):
+    """k = 1536 (24 steps, even): 128-token tiles take two steps per ring stage."""
     m, n = ragged_shape(fm, fn, 1)
-    k = 704 if fm == 2 else 644
     print(f"tile {128 * fm}x{32 * fn}: m={m} n={n} k={k}", flush=True)
     w, p_ref, g_ref, _ = make_linear(97, fm * 10 + fn, n, k)
     x = synth.activations(97, m, k, dtype="bf16", heavy_channels=max(1, k // 100))
