@@ -96,19 +96,20 @@ __device__ inline uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// s_waitcnt immediate: vmcnt <= VM, lgkmcnt = 0, expcnt untouched (gfx9 encoding)
-template <int VM>
-constexpr int waitcnt_vm_lgkm0() { return (VM & 15) | (7 << 4) | ((VM >> 4) << 14); }
+// s_waitcnt immediate: vmcnt <= VM, lgkmcnt <= LG, expcnt untouched (gfx9 encoding)
+template <int VM, int LG>
+constexpr int waitcnt_vm_lgkm() { return (VM & 15) | (7 << 4) | (LG << 8) | ((VM >> 4) << 14); }
 
-// Barrier that leaves the newest VM direct loads in flight: wait until at most
-// VM vector-memory operations of this thread are outstanding and all LDS
-// operations are done, then s_barrier. The empty asm statements keep the
-// compiler from moving memory accesses across.
-template <int VM>
+// Barrier that leaves the newest VM direct loads and the newest LG LDS reads
+// in flight: wait until at most VM vector-memory and LG LDS operations of this
+// thread are outstanding (both complete in issue order), then s_barrier. The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int VM, int LG = 0>
 __device__ inline void ring_barrier()
 {
+    static_assert(VM < 64 && LG < 16, "waitcnt fields");
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<VM>());
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm<VM, LG>());
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -413,7 +414,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         adv(ws_iss, WS, SBW * WS);
     };
     // Before the barrier that ends stage S, stage S+2 must have landed: the
-    // following stage reads (part of) it before its own barrier.
+    // following stage reads (part of) it before its own barrier. The barrier
+    // leaves the last FM LDS reads of the stage in flight: they fetch the first
+    // activation half of the next step, which lives in a ring slot the coming
+    // direct loads do not touch; every read of the slot those loads overwrite
+    // was issued earlier and has completed.
     if constexpr (SPB == 1) {
         // one barrier per step; two steps per iteration so the packed-weight
         // registers alternate without copies; no branch inside the body (a merge
@@ -425,8 +430,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                 if (issue) dma_stage(ks + DB, xs_iss, ws_iss);
             });
             advance();
-            if (issue) ring_barrier<VM_SLACK>();
-            else ring_barrier<0>();
+            if (issue) ring_barrier<VM_SLACK, FM>();
+            else ring_barrier<0, FM>();
         };
         int ks = 0;
         for (; ks + 1 < nks; ks += 2) {
@@ -445,8 +450,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             });
             step(wB, wA, xl1 + xs_cur + X_TILE, wl + ws_nxt, xl0 + xs_nxt, [] {});
             advance();
-            if (issue) ring_barrier<VM_SLACK>();
-            else ring_barrier<0>();
+            if (issue) ring_barrier<VM_SLACK, FM>();
+            else ring_barrier<0, FM>();
         }
     }
 
