@@ -39,8 +39,9 @@ __device__ inline v4i expand_codes4(uint32_t w)
                (int)((w >> 6) & 0x03030303u)};
 }
 
-// MB: 16-token blocks (1..4). EPI as for the GEMM.
-template <int MB, int EPI>
+// MB: 16-token blocks (1..4). EPI as for the GEMM. KB > 0: each wave has at
+// most KB blocks, all requested at the start.
+template <int MB, int EPI, int KB = 0>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
 {
     constexpr bool DUAL = EPI == EPI_GATE;
@@ -83,6 +84,34 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
             }
     };
 
+    if constexpr (KB > 0) {
+        // every packed-weight block of this wave requested up front (KB of them,
+        // blocks past the end are code 1 against zero activations); the
+        // activations of block i+1 are loaded while block i runs
+        v4u wv[KB][NA];
+        v4i qa[4][MB], qb[4][MB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) load_block(wave + 4 * i, wv[i], i == 0 ? qa : qb);
+        __builtin_amdgcn_sched_barrier(0);  // keep every request ahead of the first use
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            v4i (&qc)[4][MB] = (i & 1) ? qb : qa;
+            v4i (&qn)[4][MB] = (i & 1) ? qa : qb;
+            if (i + 1 < KB) {
+                v4u unused[NA];
+                load_block(wave + 4 * (i + 1), unused, qn);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int mat = 0; mat < NA; ++mat) {
+                    const v4i av = expand_codes4(wv[i][mat][s]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mat][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, qc[s][mb], acc[mat][mb], 0, 0, 0);
+                }
+        }
+    } else {
     v4u wcur[NA], wnxt[NA];
     v4i qcur[4][MB], qnxt[4][MB];
     int b = wave;
@@ -107,6 +136,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) qcur[s][mb] = qnxt[s][mb];
+    }
     }
 
     // combine the four waves' partial sums
@@ -154,14 +184,31 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
 
 bool skinny_supported(int64_t m) { return m >= 1 && m <= 64; }
 
-template <int MB>
+template <int MB, int KB = 0>
 static void launch_mb(const SkinnyArgs &a, int epi, hipStream_t st)
 {
     const dim3 grid((unsigned)ceil_div(a.n, kSkRows));
     switch (epi) {
-    case EPI_Y: hipLaunchKernelGGL((skinny_kernel<MB, EPI_Y>), grid, dim3(kThreads), 0, st, a); break;
-    case EPI_ACC: hipLaunchKernelGGL((skinny_kernel<MB, EPI_ACC>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((skinny_kernel<MB, EPI_GATE>), grid, dim3(kThreads), 0, st, a); break;
+    case EPI_Y: hipLaunchKernelGGL((skinny_kernel<MB, EPI_Y, KB>), grid, dim3(kThreads), 0, st, a); break;
+    case EPI_ACC: hipLaunchKernelGGL((skinny_kernel<MB, EPI_ACC, KB>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((skinny_kernel<MB, EPI_GATE, KB>), grid, dim3(kThreads), 0, st, a); break;
+    }
+}
+
+// up to 16 tokens: each wave's blocks (ceil(blocks / 4) of them) requested at once
+static void launch_mb1(const SkinnyArgs &a, int epi, hipStream_t st)
+{
+    const int kb = (int)ceil_div(ceil_div(a.kp / 64, 4), 4);
+    switch (kb) {
+    case 1: launch_mb<1, 1>(a, epi, st); break;
+    case 2: launch_mb<1, 2>(a, epi, st); break;
+    case 3: launch_mb<1, 3>(a, epi, st); break;
+    case 4: launch_mb<1, 4>(a, epi, st); break;
+    case 5: launch_mb<1, 5>(a, epi, st); break;
+    case 6: launch_mb<1, 6>(a, epi, st); break;
+    case 7: launch_mb<1, 7>(a, epi, st); break;
+    case 8: launch_mb<1, 8>(a, epi, st); break;
+    default: launch_mb<1>(a, epi, st); break;
     }
 }
 
@@ -172,7 +219,7 @@ hipError_t launch_skinny(const GemmProblem &p, hipStream_t st)
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw; a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out;
     switch ((p.m + 15) / 16) {
-    case 1: launch_mb<1>(a, p.epi, st); break;
+    case 1: launch_mb1(a, p.epi, st); break;
     case 2: launch_mb<2>(a, p.epi, st); break;
     case 3: launch_mb<3>(a, p.epi, st); break;
     default: launch_mb<4>(a, p.epi, st); break;

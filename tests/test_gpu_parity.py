@@ -83,6 +83,7 @@ FWD_SHAPES = [
     (1, 2560, 6913), (3, 512, 1031), (1, 16384, 300), (2, 20000, 64),            # decode: ragged blocks, long k
     (6, 2560, 6913), (7, 6912, 2561), (8, 260, 33), (8, 20000, 64), (8, 16384, 300),  # decode, 5..8 tokens
     (9, 644, 40), (12, 4100, 77), (13, 2052, 45), (16, 6912, 2561), (16, 8192, 100),  # 9..16 tokens
+    (8, 6912, 100), (16, 2560, 300),                                             # one-launch path, layer shapes
     (5, 256, 256), (17, 260, 33), (33, 512, 257), (64, 2560, 512), (65, 256, 300),  # MFMA paths
     (130, 640, 200), (300, 256, 130),
 ]
