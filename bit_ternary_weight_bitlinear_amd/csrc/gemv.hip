@@ -29,7 +29,7 @@ namespace bl {
 constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxTasks = 16;         // 16-byte weight tasks per thread and matrix
 constexpr int kGemvLdsLimit = 60 * 1024;
-constexpr int kSlots = 4;             // activation groups a thread keeps in registers
+constexpr int kSlots = 4;             // at most this many activation groups per thread in registers
 constexpr int kGT = 512;              // threads per workgroup (8 waves: two per SIMD)
 constexpr int kGW = kGT / 64;         // waves per workgroup
 
@@ -51,9 +51,10 @@ struct GemvArgs {
 // that lanes reading neighbouring chunks spread over the banks.
 __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) & 3)) << 4); }
 
-// RES: all m*ceil(k/16) activation groups fit in kSlots per thread (loaded once,
-// quantized from registers). FULL: k % 16 == 0. JM: weight tasks per thread.
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM>
+// RES: all m*ceil(k/16) activation groups fit in SL <= kSlots per thread
+// (loaded once, quantized from registers; SL is sized to the problem so that
+// unused slots hold no registers). FULL: k % 16 == 0. JM: weight tasks per thread.
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
     constexpr int NA = DUAL ? 2 : 1;
@@ -75,11 +76,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     const int NG = MT * G;
 
     // 1. activation loads first: the quantization waits only for these
-    float xr[kSlots][16];
-    int slot_t[kSlots], slot_g[kSlots];
+    float xr[SL][16];
+    int slot_t[SL], slot_g[SL];
     if constexpr (RES) {
 #pragma unroll
-        for (int s = 0; s < kSlots; ++s) {
+        for (int s = 0; s < SL; ++s) {
             const int f = min(tid + s * kGT, NG - 1);  // clamped: always a valid group
             slot_t[s] = MT == 1 ? 0 : f / G;
             slot_g[s] = f - slot_t[s] * G;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
         if constexpr (RES) {
 #pragma unroll
-            for (int s = 0; s < kSlots; ++s) {
+            for (int s = 0; s < SL; ++s) {
                 if (s * kGT < NG) {
                     float m = 0.0f;
 #pragma unroll
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         };
         if constexpr (RES) {
 #pragma unroll
-            for (int s = 0; s < kSlots; ++s) {
+            for (int s = 0; s < SL; ++s) {
                 if (tid + s * kGT < NG) {
                     float iv = inv[0];
 #pragma unroll
@@ -335,37 +336,48 @@ bool gemv_supported(int64_t m, int64_t kp)
 
 namespace {
 
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM>
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots>
 void launch_one(dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM>), grid, dim3(kGT), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL>), grid, dim3(kGT), lds, st, a);
 }
 
 // single token, whole groups, activations resident: the decode hot path, with
 // the task count per thread matched closely
-template <typename T, bool DUAL>
+template <typename T, bool DUAL, int SL>
 void launch_m1(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    if (jm <= 1) launch_one<T, 1, DUAL, true, true, 1>(grid, lds, st, a);
-    else if (jm <= 2) launch_one<T, 1, DUAL, true, true, 2>(grid, lds, st, a);
-    else if (jm <= 3) launch_one<T, 1, DUAL, true, true, 3>(grid, lds, st, a);
-    else if (jm <= 4) launch_one<T, 1, DUAL, true, true, 4>(grid, lds, st, a);
-    else if (jm <= 5) launch_one<T, 1, DUAL, true, true, 5>(grid, lds, st, a);
-    else if (jm <= 6) launch_one<T, 1, DUAL, true, true, 6>(grid, lds, st, a);
-    else if (jm <= 8) launch_one<T, 1, DUAL, true, true, 8>(grid, lds, st, a);
-    else if (jm <= 10) launch_one<T, 1, DUAL, true, true, 10>(grid, lds, st, a);
-    else if (jm <= 12) launch_one<T, 1, DUAL, true, true, 12>(grid, lds, st, a);
-    else if (jm <= 14) launch_one<T, 1, DUAL, true, true, 14>(grid, lds, st, a);
-    else launch_one<T, 1, DUAL, true, true, 16>(grid, lds, st, a);
+    if (jm <= 1) launch_one<T, 1, DUAL, true, true, 1, SL>(grid, lds, st, a);
+    else if (jm <= 2) launch_one<T, 1, DUAL, true, true, 2, SL>(grid, lds, st, a);
+    else if (jm <= 3) launch_one<T, 1, DUAL, true, true, 3, SL>(grid, lds, st, a);
+    else if (jm <= 4) launch_one<T, 1, DUAL, true, true, 4, SL>(grid, lds, st, a);
+    else if (jm <= 5) launch_one<T, 1, DUAL, true, true, 5, SL>(grid, lds, st, a);
+    else if (jm <= 6) launch_one<T, 1, DUAL, true, true, 6, SL>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<T, 1, DUAL, true, true, 8, SL>(grid, lds, st, a);
+    else if (jm <= 10) launch_one<T, 1, DUAL, true, true, 10, SL>(grid, lds, st, a);
+    else if (jm <= 12) launch_one<T, 1, DUAL, true, true, 12, SL>(grid, lds, st, a);
+    else if (jm <= 14) launch_one<T, 1, DUAL, true, true, 14, SL>(grid, lds, st, a);
+    else launch_one<T, 1, DUAL, true, true, 16, SL>(grid, lds, st, a);
 }
 
 // 2..4 tokens, whole groups, activations resident
-template <typename T, int MT, bool DUAL>
+template <typename T, int MT, bool DUAL, int SL>
 void launch_mt(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    if (jm <= 4) launch_one<T, MT, DUAL, true, true, 4>(grid, lds, st, a);
-    else if (jm <= 8) launch_one<T, MT, DUAL, true, true, 8>(grid, lds, st, a);
-    else launch_one<T, MT, DUAL, true, true, 16>(grid, lds, st, a);
+    if (jm <= 4) launch_one<T, MT, DUAL, true, true, 4, SL>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<T, MT, DUAL, true, true, 8, SL>(grid, lds, st, a);
+    else launch_one<T, MT, DUAL, true, true, 16, SL>(grid, lds, st, a);
+}
+
+template <typename T, bool DUAL, int SL>
+void launch_res(int m, int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    switch (m) {
+    case 1: launch_m1<T, DUAL, SL>(jm, grid, lds, st, a); break;
+    case 2: launch_mt<T, 2, DUAL, SL>(jm, grid, lds, st, a); break;
+    case 3: launch_mt<T, 3, DUAL, SL>(jm, grid, lds, st, a); break;
+    default: launch_mt<T, 4, DUAL, SL>(jm, grid, lds, st, a); break;
+    }
 }
 
 // anything else (k % 16 != 0, or activations too long for registers)
@@ -389,12 +401,11 @@ void dispatch(const GemvProblem &p, int jm, dim3 grid, size_t lds, hipStream_t s
         launch_generic<T, DUAL>((int)p.m, grid, lds, st, a);
         return;
     }
-    switch (p.m) {
-    case 1: launch_m1<T, DUAL>(jm, grid, lds, st, a); break;
-    case 2: launch_mt<T, 2, DUAL>(jm, grid, lds, st, a); break;
-    case 3: launch_mt<T, 3, DUAL>(jm, grid, lds, st, a); break;
-    default: launch_mt<T, 4, DUAL>(jm, grid, lds, st, a); break;
-    }
+    // resident activation slots per thread: 1, 2 or 4
+    const int64_t sl = ceil_div(p.m * ceil_div(p.k, 16), (int64_t)kGT);
+    if (sl <= 1) launch_res<T, DUAL, 1>((int)p.m, jm, grid, lds, st, a);
+    else if (sl <= 2) launch_res<T, DUAL, 2>((int)p.m, jm, grid, lds, st, a);
+    else launch_res<T, DUAL, 4>((int)p.m, jm, grid, lds, st, a);
 }
 
 }  // namespace
