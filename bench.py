@@ -237,26 +237,31 @@ def bench_layer(bl, torch, dev, steps, warmup, pool_mb):
     return out
 
 
-def bench_ffn(bl, torch, dev, steps, warmup):
+def bench_ffn(bl, torch, dev, steps, warmup, pool_mb):
     cfg = synth.WORKLOADS[5]
     hid, f = cfg["hidden"], cfg["ffn"]
-    gate = make_weights(bl, torch, 5, "gate", f, hid, dev)
-    up = make_weights(bl, torch, 5, "up", f, hid, dev)
-    down = make_weights(bl, torch, 5, "down", hid, f, dev)
+    mats = [make_weights(bl, torch, 5, "gate", f, hid, dev), make_weights(bl, torch, 5, "up", f, hid, dev),
+            make_weights(bl, torch, 5, "down", hid, f, dev)]
     packed_bytes = 3 * f * hid // 4
     out = {}
     for m in cfg["ms"]:
+        # one token: the weights rotate through distinct copies (cold from HBM,
+        # as for decode); 2048 tokens: compute-bound, one copy
+        pool, pool_bytes = rotation_pool(torch, mats, pool_mb << 20) if m == 1 else ([mats], packed_bytes)
         x = act_tensor(torch, 5, m, hid, dev)
         ws = torch.empty(bl.workspace_size(bl.OP_FFN, m, hid, f), dtype=torch.uint8, device=dev)
 
         def step(i):
-            bl.ffn(x, gate, up, down, workspace=ws)
+            g, u, d = pool[i % len(pool)]
+            bl.ffn(x, g, u, d, workspace=ws)
 
         for i in range(warmup):
             step(i)
-        t, _ = Timer(torch).graph_region(step, steps, min(steps, 8))
+        t, _ = Timer(torch).graph_region(step, steps, len(pool) if m == 1 else min(steps, 8))
         ops = 2.0 * m * 3 * f * hid
-        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9, tops=ops / t / 1e12)
+        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9, tops=ops / t / 1e12,
+                            pool_bytes=pool_bytes)
+        del pool
     return out
 
 
@@ -357,7 +362,7 @@ def main():
     if args.workload == "all":
         extra["batched_decode_layer"] = bench_layer(bl, torch, dev, args.steps, args.warmup, args.pool_mb)
         log("layer:", json.dumps(extra["batched_decode_layer"]))
-        extra["ffn_8b"] = bench_ffn(bl, torch, dev, max(10, args.steps // 10), max(3, args.warmup // 5))
+        extra["ffn_8b"] = bench_ffn(bl, torch, dev, max(10, args.steps // 10), max(3, args.warmup // 5), args.pool_mb)
         log("ffn:", json.dumps(extra["ffn_8b"]))
 
     achieved = dec["algo_bytes_per_launch"] / dec["kernel_mean_s"] / 1e9

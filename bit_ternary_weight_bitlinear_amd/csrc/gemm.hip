@@ -126,7 +126,8 @@ __device__ inline uint64_t shr64(uint64_t v)
     return r;
 }
 
-// Epilogue of one wave: y = (float)(acc - sumq) * ((s / 127) * gamma) for its
+// Epilogue of one wave (non-temporal stores: the output is not read back by
+// this kernel): y = (float)(acc - sumq) * ((s / 127) * gamma) for its
 // 32*FM tokens (tile rows wave*32*FM ..) x 32*FN features. tok_sq / tok_s hold
 // sum_k q and s of the tile's tokens (LDS). Interior tiles store without bounds
 // checks, one row pointer per token and immediate offsets per block.
@@ -178,9 +179,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
                             float o;
                             if constexpr (DUAL) o = sq_relu_gate((float)va * c0e[e], (float)(acc[NA - 1][fm][fn][4 * j + e] - sq[e]) * c1e[e]);
                             else o = (float)va * c0e[e];
-                            out[row + fn * 32] = o;
+                            __builtin_nontemporal_store(o, &out[row + fn * 32]);
                         }
-                        if constexpr (ACC) acc_out[row + fn * 32] = va;
+                        if constexpr (ACC) __builtin_nontemporal_store(va, &acc_out[row + fn * 32]);
                     }
                 }
             }
