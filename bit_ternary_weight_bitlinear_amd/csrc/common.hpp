@@ -60,6 +60,15 @@ __device__ inline float wave_max(float v)
     return v;
 }
 
+// sum over each group of 8 lanes (8i .. 8i+7); every lane of the group gets it
+__device__ inline int group8_sum(int v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    v += dpp_mov<kDppRowHalfMirror>(v);
+    return v;
+}
+
 __device__ inline int wave_sum(int v)
 {
     v += dpp_mov<kDppQuadXor1>(v);

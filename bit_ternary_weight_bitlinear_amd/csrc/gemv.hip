@@ -4,13 +4,17 @@
 // stream over the packed weights: 2 bits per weight is the whole HBM traffic.
 // Design:
 //  * one workgroup per CU: workgroup b owns rows [b*R, b*R + R) with
-//    R = ceil(n / 256), a contiguous block of R * k/4 bytes, cut into 16-byte
-//    tasks (64 weights of one row) handed to the 512 threads round-robin, row
-//    index fastest. Every CU reads the same number of bytes, and every CU does
-//    the activation quantization below exactly once;
+//    R = ceil(n / 256), a contiguous block of R * k/4 bytes. Each row is cut
+//    into blocks of eight 16-byte chunks (512 weights); a group of 8 lanes
+//    takes one (row, block) unit and each lane one chunk, so every group reads
+//    128 contiguous bytes and a wave's 8 groups read the same block of 8 rows
+//    (the activation chunks they need are then shared: LDS broadcast). Units
+//    go to the 64 groups round-robin, row index fastest. Every CU reads the
+//    same number of bytes and does the activation quantization below once;
 //  * each thread first issues its activation loads, then all of its weight
-//    loads (a compile-time count, no branches), so everything is in flight at
-//    once and the quantization can start as soon as the activations arrive;
+//    loads (a compile-time count; waves with no unit in a round skip it), so
+//    everything is in flight at once and the quantization can start as soon
+//    as the activations arrive;
 //  * the workgroup quantizes the m tokens itself (absmax with DPP wave
 //    reductions, round by the 1.5*2^23 add) into LDS in the qperm order: no
 //    separate activation kernel, no launch gap;
@@ -18,7 +22,8 @@
 //    dword (code<<0, <<2, <<4 and, after a right shift by one, <<5 -- each fits a
 //    signed byte) and fed to v_dot4_i32_i8 against the qperm dwords; the four
 //    partial sums are brought back to scale by exact shifts;
-//  * per-task sums are added into per-row int32 accumulators in LDS
+//  * the 8 lane sums of a unit are added with DPP inside the group, and one
+//    lane adds the unit's sum into its row's int32 accumulator in LDS
 //    (ds_add_u32); integer sums are exact, so the order of the adds does not
 //    matter and the result is deterministic.
 #include "common.hpp"
@@ -27,7 +32,7 @@
 namespace bl {
 
 constexpr int kNumCUs = 256;          // MI355X: 8 XCDs x 32 CUs
-constexpr int kMaxTasks = 16;         // 16-byte weight tasks per thread and matrix
+constexpr int kMaxUnits = 1024;       // (row, 8-chunk block) units per workgroup and matrix
 constexpr int kGemvLdsLimit = 60 * 1024;
 constexpr int kSlots = 4;             // at most this many activation groups per thread in registers
 constexpr int kGT = 512;              // threads per workgroup (8 waves: two per SIMD)
@@ -69,7 +74,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     const int R = a.rows_per_wg, C = a.chunks;
     const int64_t r0 = (int64_t)blockIdx.x * R;
     const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
-    const int ntask = rows * C;
     const T *x = static_cast<const T *>(a.x);
     const int G = (int)ceil_div(a.k, 16);
     const int GP = (int)(a.kp / 16);
@@ -89,31 +93,37 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         }
     }
 
-    // 2. the weight tasks of this thread: task f = tid + 256*j is (row f % rows,
-    //    chunk f / rows); tasks past the end repeat the last one (sums dropped)
+    // 2. the weight units of this thread: unit u = group + 64*j is (row u % rows,
+    //    block u / rows); lane l of the group takes chunk 8*block + l. Lanes past
+    //    the row's last chunk (and whole units past the end) re-read chunk C-1 of
+    //    a row of this workgroup; their sums are dropped.
+    const int grp = tid >> 3, li = tid & 7;
     int tr[JM], tc[JM];
+    bool tv[JM];
     {
-        const int last = ntask - 1;
-        const int lc = last / rows, lr = last - lc * rows;
-        const int dc = kGT / rows, dr = kGT - dc * rows;
-        int c = tid / rows;
-        int r = tid - c * rows;
+        const int db = (kGT / 8) / rows, dr = (kGT / 8) - db * rows;
+        int b = grp / rows;
+        int r = grp - b * rows;
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
-            const bool ok = tid + j * kGT < ntask;
-            tr[j] = ok ? r : lr;
-            tc[j] = ok ? c : lc;
+            const int c = 8 * b + li;
+            tv[j] = c < C;
+            tr[j] = r;
+            tc[j] = c < C ? c : C - 1;
             r += dr;
-            c += dc;
+            b += db;
             if (r >= rows) {
                 r -= rows;
-                c += 1;
+                b += 1;
             }
         }
     }
+    const int nunit = rows * ((C + 7) >> 3);
     uint4 wa[JM], wb[JM];
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
+        // uniform per wave: waves with no unit in this round load nothing
+        if (wave * 8 + j * (kGT / 8) >= nunit) continue;
         const int64_t off = (r0 + tr[j]) * a.ldw + (int64_t)tc[j] * 16;
         wa[j] = load_nt16(a.w0 + off);
         if constexpr (DUAL) wb[j] = load_nt16(a.w1 + off);
@@ -224,10 +234,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     }
 
     // 4. decode the 2-bit codes in registers, v_dot4 against the qperm dwords,
-    //    add each task's sum into its row's LDS accumulator
+    //    sum each unit over its 8 lanes and add it into its row's LDS accumulator
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
-        if (tid + j * kGT < ntask) {
+        // uniform per wave: the wave's first unit of this round exists
+        if (wave * 8 + j * (kGT / 8) < nunit) {
             const int c = tc[j];
             int acc[MT][4], accb[MT][4];
 #pragma unroll
@@ -270,14 +281,20 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
                     }
                 }
             }
+            // lane 0 of the group holds chunk 8*block, so its flag says whether
+            // the unit exists
+            const bool add = li == 0 && tv[j];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 // undo the field shifts (each partial is an exact multiple)
-                atomicAdd(&acc_lds[t * R + tr[j]],
-                          acc[t][0] + (acc[t][1] >> 2) + (acc[t][2] >> 4) + (acc[t][3] >> 5));
-                if constexpr (DUAL)
-                    atomicAdd(&acc_lds[(MT + t) * R + tr[j]],
-                              accb[t][0] + (accb[t][1] >> 2) + (accb[t][2] >> 4) + (accb[t][3] >> 5));
+                int va = acc[t][0] + (acc[t][1] >> 2) + (acc[t][2] >> 4) + (acc[t][3] >> 5);
+                va = group8_sum(tv[j] ? va : 0);
+                if (add) atomicAdd(&acc_lds[t * R + tr[j]], va);
+                if constexpr (DUAL) {
+                    int vb = accb[t][0] + (accb[t][1] >> 2) + (accb[t][2] >> 4) + (accb[t][3] >> 5);
+                    vb = group8_sum(tv[j] ? vb : 0);
+                    if (add) atomicAdd(&acc_lds[(MT + t) * R + tr[j]], vb);
+                }
             }
         }
     }
@@ -305,17 +322,23 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 
 // ---------------------------------------------------------------- host side
 
-// Rows per workgroup: one workgroup per CU while that keeps each thread at <= 4
-// weight loads (counting both matrices of a gate/up pair); larger matrices are
-// split further so more workgroups share a CU and hide each other's latency.
-constexpr int kTargetLoads = 4;
+// Rows per workgroup: one workgroup per CU while that keeps each thread at
+// about 8 weight loads or fewer (counting both matrices of a gate/up pair);
+// larger matrices are split further so more workgroups share a CU. Fewer,
+// larger workgroups repeat the activation prologue less often: with at most
+// 4 loads per thread the 8B FFN at one token took ~0.4 us longer.
+constexpr int kTargetLoads = 8;
+
+// (row, 8-chunk block) units per row, and the most rows a workgroup may own
+static int64_t gemv_blocks(int64_t chunks) { return ceil_div(chunks, (int64_t)8); }
+static int64_t gemv_rows_max(int64_t chunks) { return kMaxUnits / gemv_blocks(chunks); }
 
 static int64_t gemv_rows_per_wg(int64_t n, int64_t chunks, bool dual)
 {
     int64_t r = ceil_div(n, kNumCUs);
     const int64_t na = dual ? 2 : 1;
     while (r > 1 && r * chunks * na > (int64_t)kTargetLoads * kGT) r = ceil_div(r, 2);
-    const int64_t rmax = (int64_t)kMaxTasks * kGT / chunks;  // tasks per thread <= 16
+    const int64_t rmax = gemv_rows_max(chunks);  // units per workgroup <= kMaxUnits
     if (r > rmax) r = rmax;
     return r < 1 ? 1 : r;
 }
@@ -328,9 +351,9 @@ static size_t gemv_lds_bytes(int64_t m, int64_t kp, int64_t r, bool dual)
 bool gemv_supported(int64_t m, int64_t kp)
 {
     const int64_t chunks = kp / 64;
-    if (m < 1 || m > 4 || chunks > (int64_t)kMaxTasks * kGT) return false;
-    // worst case over n: rows per workgroup is at most 16*256/chunks
-    const int64_t rmax = (int64_t)kMaxTasks * kGT / chunks;
+    if (m < 1 || m > 4 || gemv_blocks(chunks) > kMaxUnits) return false;
+    // worst case over n: the most rows a workgroup may own
+    const int64_t rmax = gemv_rows_max(chunks);
     return gemv_lds_bytes(m, kp, rmax, true) <= (size_t)kGemvLdsLimit;
 }
 
@@ -421,7 +444,7 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     const bool dual = p.w1 != nullptr;
     const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);
     a.rows_per_wg = (int)r;
-    const int jm = (int)ceil_div(r * a.chunks, kGT);
+    const int jm = (int)ceil_div(r * gemv_blocks(a.chunks), (int64_t)(kGT / 8));
     const dim3 grid((unsigned)ceil_div(p.n, r));
     const size_t lds = gemv_lds_bytes(p.m, p.kp, r, dual);
     if (p.bf16) {
