@@ -12,9 +12,8 @@
 //    go to the 64 groups round-robin, row index fastest. Every CU reads the
 //    same number of bytes and does the activation quantization below once;
 //  * each thread first issues its activation loads, then all of its weight
-//    loads (a compile-time count; waves with no unit in a round skip it), so
-//    everything is in flight at once and the quantization can start as soon
-//    as the activations arrive;
+//    loads (a compile-time count, no branches), so everything is in flight at
+//    once and the quantization can start as soon as the activations arrive;
 //  * the workgroup quantizes the m tokens itself (absmax with DPP wave
 //    reductions, round by the 1.5*2^23 add) into LDS in the qperm order: no
 //    separate activation kernel, no launch gap;
@@ -52,6 +51,31 @@ struct GemvArgs {
     int chunks;       // kp / 64
 };
 
+// The 16 inputs of one group from its raw 16-byte words (bf16: 2, fp32: 4).
+template <typename T>
+__device__ inline void unpack_group(const uint4 *v, float f[16])
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[4 * j + 0] = __uint_as_float(v[j].x);
+            f[4 * j + 1] = __uint_as_float(v[j].y);
+            f[4 * j + 2] = __uint_as_float(v[j].z);
+            f[4 * j + 3] = __uint_as_float(v[j].w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
+                f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
 // LDS slot of activation group (c, d): 16-byte slots rotated by (c >> 2) & 3 so
 // that lanes reading neighbouring chunks spread over the banks.
 __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) & 3)) << 4); }
@@ -79,18 +103,36 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     const int GP = (int)(a.kp / 16);
     const int NG = MT * G;
 
-    // 1. activation loads first: the quantization waits only for these
-    float xr[SL][16];
+    // 1. activation loads first: the quantization waits only for these. They
+    //    are kept as raw words and, for a small weight share per thread,
+    //    converted only after the weight loads are issued, so both are in
+    //    flight together. With a large share (6 or more 16-byte loads, the 8B
+    //    FFN matrices) the activations are converted, i.e. waited for, before
+    //    the weights are requested: otherwise they queue behind the weights
+    //    and the quantization ends later (measured: ~0.3 us per launch either
+    //    way). Every slot is loaded (clamped to a valid group), with no branch.
+    constexpr bool kActFirst = JM * NA >= 6;
+    constexpr int XQ = (int)sizeof(T) * 16 / 16;  // 16-byte words per group
+    uint4 xq[SL][XQ];
     int slot_t[SL], slot_g[SL];
     if constexpr (RES) {
 #pragma unroll
         for (int s = 0; s < SL; ++s) {
-            const int f = min(tid + s * kGT, NG - 1);  // clamped: always a valid group
+            const int f = min(tid + s * kGT, NG - 1);
             slot_t[s] = MT == 1 ? 0 : f / G;
             slot_g[s] = f - slot_t[s] * G;
-            if (s * kGT < NG)  // uniform: slots no thread needs are not loaded
-                load_group<T, FULL>(x + slot_t[s] * a.k, a.k, slot_g[s], xr[s]);
+            const uint4 *p = reinterpret_cast<const uint4 *>(x + slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
         }
+    }
+    float xr[SL][16];
+    if constexpr (RES && kActFirst) {
+        // only the activation loads are outstanding here
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < SL; ++s) unpack_group<T>(xq[s], xr[s]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // 2. the weight units of this thread: unit u = group + 64*j is (row u % rows,
@@ -119,11 +161,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         }
     }
     const int nunit = rows * ((C + 7) >> 3);
+    // every slot is loaded, with no branch between the loads, so the waits
+    // below can count them and the products of a unit start when its own
+    // weights have arrived
     uint4 wa[JM], wb[JM];
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
-        // uniform per wave: waves with no unit in this round load nothing
-        if (wave * 8 + j * (kGT / 8) >= nunit) continue;
         const int64_t off = (r0 + tr[j]) * a.ldw + (int64_t)tc[j] * 16;
         wa[j] = load_nt16(a.w0 + off);
         if constexpr (DUAL) wb[j] = load_nt16(a.w1 + off);
@@ -133,6 +176,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. per-token absmax, then int8 codes into LDS in the qperm order
+    if constexpr (RES && !kActFirst) {
+#pragma unroll
+        for (int s = 0; s < SL; ++s) unpack_group<T>(xq[s], xr[s]);
+    }
     float st[MT], inv[MT];
     int sq[MT];
     {
