@@ -86,6 +86,7 @@ FWD_SHAPES = [
     (8, 6912, 100), (16, 2560, 300),                                             # one-launch path, layer shapes
     (5, 256, 256), (17, 260, 33), (33, 512, 257), (64, 2560, 512), (65, 256, 300),  # MFMA paths
     (130, 640, 200), (300, 256, 130),
+    (1, 256, 40000), (2, 512, 20000),  # decode: more than 64 rows per workgroup, one 8-chunk block per row
 ]
 
 
@@ -189,7 +190,8 @@ def _ffn_case(bl, cfg, m, hid, f, sample=None, dtype="bf16"):
 
 
 @pytest.mark.parametrize("m,hid,f", [(1, 256, 512), (3, 260, 516), (4, 512, 1024), (5, 256, 512),
-                                     (33, 260, 516), (130, 512, 768)])
+                                     (33, 260, 516), (130, 512, 768),
+                                     (1, 256, 20000)])  # gate/up pair with more than 64 rows per workgroup
 def test_ffn_small(bl, m, hid, f):
     _ffn_case(bl, 96, m, hid, f)
 
