@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.hip", "pack.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "skinny.hip"]
+SOURCES = ["api.hip", "pack.hip", "act_quant.hip", "gemv.hip", "bgemv.hip", "gemm.hip", "skinny.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

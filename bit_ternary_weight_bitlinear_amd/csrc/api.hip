@@ -203,8 +203,19 @@ bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k, cons
         p.out = y; p.acc_out = acc_out;
         return hip_status(launch_gemv(p, st));
     }
+    const int bmode = bgemv_mode(m, k, dtype == BL_BF16);
+    GemvProblem bp{};
+    bp.x = x; bp.bf16 = dtype == BL_BF16; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
+    bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma;
+    bp.out = y; bp.acc_out = acc_out;
+    if (bmode == 1)  // 5..16 tokens: quantization, products and rescale in one launch
+        return hip_status(launch_bgemv(bp, st));
     if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, k, L.kp, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
+    if (bmode == 2) {  // 5..16 tokens, quantized rows from the kernel above
+        bp.x = L.qp; bp.pre_s = L.s; bp.pre_sumq = L.sumq;
+        return hip_status(launch_bgemv(bp, st));
+    }
     GemmProblem g{};
     g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;

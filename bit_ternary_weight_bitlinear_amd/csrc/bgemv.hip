@@ -1,0 +1,367 @@
+// bgemv.hip -- BitLinear for 5..16 tokens (batched decode) on gfx950, one
+// launch per matrix.
+//
+// The W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端) at a few
+// tokens is still a stream over the packed weights. This kernel keeps the
+// decode GEMV's structure -- one workgroup per CU owning a block of rows, all
+// of its weight loads in flight at once, the tokens quantized by the
+// workgroup itself -- and does the products on the int8 matrix cores:
+//  * workgroup b owns rows [b*R, b*R + R), R = min(ceil(n / 256), 32), as one
+//    or two 16-row blocks; with two blocks, even waves take block 0 and odd
+//    waves block 1, and the waves of a block split k in quads of four 64-input
+//    chunks;
+//  * per quad, lane (h, r) = (lane / 16, lane % 16) loads the 16 packed bytes
+//    of chunk 4*quad + h of row 16*block + r (rows past R re-read row R-1, so
+//    the request merges with a valid lane's) and feeds dword s of it, expanded
+//    in registers, as operand A of v_mfma_i32_16x16x64_i8 step s; operand B is
+//    the 16 qperm bytes of token r at the same inputs, read from LDS;
+//  * for m*k up to 32768 the m tokens are quantized once per workgroup, from
+//    raw words loaded before the weights and converted after the weight loads
+//    are issued: a per-token absmax (16-lane DPP maxima over the at most two
+//    tokens a wave's 64 groups touch, merged by LDS atomics), one division per
+//    token, then codes into LDS in qperm order (rows of kp + 16 bytes: the 16
+//    rows of one read phase fall on different banks) and sum_k q per token.
+//    Larger m*k would cost every workgroup too much arithmetic (2 us of VALU
+//    per CU at 8 x 6912 inputs); there the quantization kernel runs first and
+//    this one copies its int8 rows, scales and sums into LDS instead (PREQ);
+//  * the waves' partial 16x16 blocks meet in LDS; the epilogue subtracts
+//    sum_k q, rescales, stores y (and the int32 sums if asked).
+// Integer sums are exact, so the split over waves and the order of the adds
+// do not change results.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bl {
+
+constexpr int kBT = 512;       // threads per workgroup (8 waves)
+constexpr int kBW = kBT / 64;  // waves per workgroup
+constexpr int kBMaxTok = 16;   // one 16-token MFMA block
+constexpr int kBMaxRows = 32;  // at most two 16-row blocks per workgroup
+constexpr int kBMaxK = 8192;
+
+struct BgemvArgs {
+    const void *x;  // bf16 / fp32 activations, or (PREQ) qperm int8 rows of kp bytes
+    const float *pre_s;
+    const int32_t *pre_sumq;
+    int64_t m, k, kp, n;
+    const uint8_t *w;
+    int64_t ldw;
+    const float *gamma;
+    float *out;
+    int32_t *acc_out;
+    int rows_per_wg;  // R
+    int chunks;       // kp / 64
+};
+
+__device__ inline v4i bg_expand4(uint32_t w)
+{
+    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+               (int)((w >> 6) & 0x03030303u)};
+}
+
+// The 16 inputs of one group from its raw 16-byte words (bf16: 2, fp32: 4).
+template <typename T>
+__device__ inline void bg_unpack(const uint4 *v, float f[16])
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[4 * j + 0] = __uint_as_float(v[j].x);
+            f[4 * j + 1] = __uint_as_float(v[j].y);
+            f[4 * j + 2] = __uint_as_float(v[j].z);
+            f[4 * j + 3] = __uint_as_float(v[j].w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
+                f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
+// maximum / sum over each row of 16 lanes (every lane of the row gets it)
+__device__ inline float row16_max(float v)
+{
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v))));
+    return v;
+}
+__device__ inline int row16_sum(int v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    v += dpp_mov<kDppRowHalfMirror>(v);
+    v += dpp_mov<kDppRowMirror>(v);
+    return v;
+}
+
+// RB: 16-row blocks per workgroup (1 or 2). JM: quads per wave. SL: activation
+// groups of 16 inputs per thread (covering all m * k / 16 of them), or with
+// PREQ 16-byte words of the quantized rows (all m * kp / 16 of them).
+template <typename T, int RB, int JM, int SL, bool PREQ>
+__global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
+{
+    extern __shared__ __align__(16) int8_t lds[];  // q [m][kp + 16], then partial sums [kBW][4][64]
+    __shared__ unsigned tok_max[kBMaxTok];
+    __shared__ int tok_sum[kBMaxTok];
+    __shared__ float tok_inv[kBMaxTok], tok_s[kBMaxTok];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lh = lane >> 4;
+    const int M = (int)a.m;
+    const int R = a.rows_per_wg, C = a.chunks;
+    const int QS = (int)a.kp + 16;  // LDS bytes per token row
+    int8_t *q_lds = lds;
+    int *part = reinterpret_cast<int *>(lds + M * QS);
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
+    const T *x = static_cast<const T *>(a.x);
+    const int GP = (int)(a.kp / 16);
+    const int G = PREQ ? GP : (int)(a.k / 16);  // fused: k % 16 == 0
+    const int NG = M * G;
+
+    if (tid < kBMaxTok) {
+        tok_max[tid] = 0u;
+        tok_sum[tid] = 0;
+    }
+
+    // 1. activation loads (raw words); slots no thread needs are not loaded
+    //    (the condition is uniform)
+    constexpr int XQ = PREQ ? 1 : (int)sizeof(T);  // 16-byte words per group
+    uint4 xq[SL][XQ];
+    int slot_t[SL], slot_g[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+        const int f = min(tid + s * kBT, NG - 1);
+        slot_t[s] = f / G;
+        slot_g[s] = f - slot_t[s] * G;
+        if (s * kBT < NG) {
+            const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) + (int64_t)slot_t[s] * a.kp + 16 * (int64_t)slot_g[s])
+                                  : reinterpret_cast<const uint4 *>(x + (int64_t)slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) xq[s][q] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. weight quads of this wave: quad wave / RB + (kBW / RB) * j of row block
+    //    wave % RB; slots past the last quad re-read the last one (dropped)
+    const int rb = wave % RB;
+    const int nq = (C + 3) >> 2;
+    const int rr = min(16 * rb + lr, rows - 1);
+    const uint8_t *wrow = a.w + (r0 + rr) * a.ldw;
+    v4u wv[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int cq = min(wave / RB + (kBW / RB) * j, nq - 1);
+        const int c = min(4 * cq + lh, C - 1);
+        wv[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(wrow + c * 16));
+        // issue order = use order, so each quad waits only for its own load
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if constexpr (PREQ) {
+        // 3-4. the quantized rows into LDS, their scales and sums
+        if (tid < M) {
+            tok_s[tid] = a.pre_s[tid];
+            tok_sum[tid] = a.pre_sumq[tid];
+        }
+#pragma unroll
+        for (int s = 0; s < SL; ++s)
+            if (tid + s * kBT < NG)
+                *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = xq[s][0];
+        __syncthreads();
+    } else {
+    // 3. per-token absmax. The 64 groups of one wave and slot belong to at most
+    //    two tokens (t0 and t0 + 1: a token has G >= 64 groups); each 16-lane
+    //    row reduces both with DPP and its lane 0 merges them into the tokens'
+    //    maxima (integer max of non-negative float bits).
+    __syncthreads();  // tok_max / tok_sum cleared
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+        const int f0 = wave * 64 + s * kBT;  // first group of this wave and slot
+        if (f0 >= NG) continue;              // uniform
+        float xr[16];
+        bg_unpack<T>(xq[s], xr);
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xr[j]));
+        const bool valid = tid + s * kBT < NG;
+        const int t0 = f0 / G;
+        const float m0 = row16_max(valid && slot_t[s] == t0 ? mx : 0.0f);
+        const float m1 = row16_max(valid && slot_t[s] != t0 ? mx : 0.0f);
+        if (lr == 0) {
+            atomicMax(&tok_max[t0], __float_as_uint(m0));
+            if (t0 + 1 < M) atomicMax(&tok_max[t0 + 1], __float_as_uint(m1));
+        }
+    }
+    __syncthreads();
+    if (tid < M) {
+        const float st = fmaxf(__uint_as_float(tok_max[tid]), kEps);
+        tok_s[tid] = st;
+        tok_inv[tid] = 127.0f / st;
+    }
+    __syncthreads();
+
+    // 4. codes into LDS (qperm order) and sum_k q per token; padding inputs of
+    //    each token row (k .. kp) are zero
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+        const int f0 = wave * 64 + s * kBT;
+        if (f0 >= NG) continue;
+        const bool valid = tid + s * kBT < NG;
+        int sum = 0;
+        if (valid) {
+            float xr[16];
+            bg_unpack<T>(xq[s], xr);
+            uint4 pv;
+            sum = quant_group(xr, tok_inv[slot_t[s]], &pv, nullptr);
+            *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = pv;
+        }
+        const int t0 = f0 / G;
+        const int s0 = row16_sum(valid && slot_t[s] == t0 ? sum : 0);
+        const int s1 = row16_sum(valid && slot_t[s] != t0 ? sum : 0);
+        if (lr == 0) {
+            atomicAdd(&tok_sum[t0], s0);
+            if (t0 + 1 < M) atomicAdd(&tok_sum[t0 + 1], s1);
+        }
+    }
+    for (int i = tid; i < M * (GP - G); i += kBT) {
+        const int t = i / (GP - G), g = G + (i - t * (GP - G));
+        *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    }
+
+    // 5. products: per quad, four MFMAs (dword s of each lane's 16 packed bytes
+    //    against the qperm bytes of token lr at the same inputs); tokens past m
+    //    and chunks past the row contribute zero
+    v4i acc = v4i{0, 0, 0, 0};
+    const int lt = lr < M ? lr : 0;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+        const int cq = wave / RB + (kBW / RB) * j;
+        if (cq < nq) {  // uniform
+            const int c = 4 * cq + lh;
+            const bool ok = c < C && lr < M;
+            const int cc = c < C ? c : C - 1;
+            const int8_t *qrow = q_lds + lt * QS + cc * 64;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v4i qv = *reinterpret_cast<const v4i *>(qrow + s * 16);
+                const v4i bq = ok ? qv : v4i{0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(bg_expand4(wv[j][s]), bq, acc, 0, 0, 0);
+            }
+        }
+    }
+    // C[row][token]: lane (h, r) holds rows 4h + v (v = 0..3) of token r
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[(wave * 4 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+
+    // 6. epilogue: thread -> (row block, register v, lane), summed over the
+    //    waves of its row block
+    if (tid < RB * 256) {
+        const int eb = tid >> 8, v = (tid >> 6) & 3, el = tid & 63;
+        const int row = 16 * eb + 4 * (el >> 4) + v, t = el & 15;
+        if (row < rows && t < M) {
+            int va = -tok_sum[t];
+#pragma unroll
+            for (int w = eb; w < kBW; w += RB) va += part[(w * 4 + v) * 64 + el];
+            const int64_t o = (int64_t)t * a.n + r0 + row;
+            a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0]);
+            if (a.acc_out) a.acc_out[o] = va;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+static int bgemv_slots(int64_t words) { return (int)ceil_div(words, (int64_t)kBT); }
+
+int bgemv_mode(int64_t m, int64_t k, bool bf16)
+{
+    if (m < 5 || m > kBMaxTok || k > kBMaxK) return 0;
+    // fused: whole 16-input groups, at least 64 of them per token (a wave's
+    // groups touch two tokens at most) and few enough inputs that every
+    // workgroup may quantize them all
+    if (k % 16 == 0 && k >= 1024 && m * k <= 32768 && bgemv_slots(m * k / 16) <= (bf16 ? 8 : 4)) return 1;
+    return bgemv_slots(m * round_up(k, 64) / 16) <= 8 ? 2 : 0;
+}
+
+namespace {
+
+template <typename T, int RB, int JM, int SL, bool PREQ>
+hipError_t bg_launch(dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
+{
+    auto kern = bgemv_kernel<T, RB, JM, SL, PREQ>;
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
+        return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kBT), lds, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int RB, int SL, bool PREQ>
+hipError_t bg_jm(int jm, dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
+{
+    if (jm <= 1) return bg_launch<T, RB, 1, SL, PREQ>(grid, lds, st, a);
+    if (jm <= 2) return bg_launch<T, RB, 2, SL, PREQ>(grid, lds, st, a);
+    if (jm <= 3) return bg_launch<T, RB, 3, SL, PREQ>(grid, lds, st, a);
+    if (jm <= 4) return bg_launch<T, RB, 4, SL, PREQ>(grid, lds, st, a);
+    if (jm <= 6) return bg_launch<T, RB, 6, SL, PREQ>(grid, lds, st, a);
+    return bg_launch<T, RB, 8, SL, PREQ>(grid, lds, st, a);
+}
+
+template <typename T, int SL, bool PREQ>
+hipError_t bg_rb(int rb, int jm, dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
+{
+    return rb == 1 ? bg_jm<T, 1, SL, PREQ>(jm, grid, lds, st, a) : bg_jm<T, 2, SL, PREQ>(jm, grid, lds, st, a);
+}
+
+}  // namespace
+
+hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
+{
+    BgemvArgs a;
+    const bool preq = p.pre_s != nullptr;
+    a.x = p.x; a.pre_s = p.pre_s; a.pre_sumq = p.pre_sumq;
+    a.m = p.m; a.k = p.k; a.kp = p.kp; a.n = p.n;
+    a.w = p.w0; a.ldw = p.ldw; a.gamma = p.gamma0;
+    a.out = p.out; a.acc_out = p.acc_out;
+    a.chunks = (int)(p.kp / 64);
+    int64_t r = ceil_div(p.n, (int64_t)256);
+    if (r > kBMaxRows) r = kBMaxRows;
+    a.rows_per_wg = (int)r;
+    const int rb = r > 16 ? 2 : 1;
+    const int64_t nq = ceil_div((int64_t)a.chunks, (int64_t)4);
+    const int jm = (int)ceil_div(nq, (int64_t)(kBW / rb));  // <= 8: kp <= 8192
+    const dim3 grid((unsigned)ceil_div(p.n, r));
+    const size_t lds = (size_t)p.m * (p.kp + 16) + (size_t)kBW * 4 * 64 * 4;
+    if (preq) {
+        const int sl = bgemv_slots(p.m * p.kp / 16);
+        if (sl <= 2) return bg_rb<int8_t, 2, true>(rb, jm, grid, lds, st, a);
+        if (sl <= 4) return bg_rb<int8_t, 4, true>(rb, jm, grid, lds, st, a);
+        return bg_rb<int8_t, 8, true>(rb, jm, grid, lds, st, a);
+    }
+    const int sl = bgemv_slots(p.m * p.k / 16);
+    if (p.bf16) {
+        if (sl <= 2) return bg_rb<bf16_t, 2, false>(rb, jm, grid, lds, st, a);
+        if (sl <= 4) return bg_rb<bf16_t, 4, false>(rb, jm, grid, lds, st, a);
+        return bg_rb<bf16_t, 8, false>(rb, jm, grid, lds, st, a);
+    }
+    if (sl <= 2) return bg_rb<float, 2, false>(rb, jm, grid, lds, st, a);
+    return bg_rb<float, 4, false>(rb, jm, grid, lds, st, a);
+}
+
+}  // namespace bl
