@@ -1,5 +1,4 @@
-// bgemv.hip -- BitLinear for 5..16 tokens (batched decode) on gfx950, one
-// launch per matrix.
+// bgemv.hip -- BitLinear for 5..32 tokens (batched decode) on gfx950.
 //
 // The W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端) at a few
 // tokens is still a stream over the packed weights. This kernel keeps the
@@ -14,7 +13,8 @@
 //    of chunk 4*quad + h of row 16*block + r (rows past R re-read row R-1, so
 //    the request merges with a valid lane's) and feeds dword s of it, expanded
 //    in registers, as operand A of v_mfma_i32_16x16x64_i8 step s; operand B is
-//    the 16 qperm bytes of token r at the same inputs, read from LDS;
+//    the 16 qperm bytes of token r (of each 16-token block: 17..32 tokens run
+//    two MFMAs per operand) at the same inputs, read from LDS;
 //  * for m*k up to 32768 the m tokens are quantized once per workgroup, from
 //    raw words loaded before the weights and converted after the weight loads
 //    are issued: a per-token absmax (16-lane DPP maxima over the at most two
@@ -22,8 +22,9 @@
 //    token, then codes into LDS in qperm order (rows of kp + 16 bytes: the 16
 //    rows of one read phase fall on different banks) and sum_k q per token.
 //    Larger m*k would cost every workgroup too much arithmetic (2 us of VALU
-//    per CU at 8 x 6912 inputs); there the quantization kernel runs first and
-//    this one copies its int8 rows, scales and sums into LDS instead (PREQ);
+//    per CU at 8 x 6912 inputs); there, and for 17..32 tokens, the
+//    quantization kernel runs first and this one copies its int8 rows, scales
+//    and sums into LDS instead (PREQ);
 //  * the waves' partial 16x16 blocks meet in LDS; the epilogue subtracts
 //    sum_k q, rescales, stores y (and the int32 sums if asked).
 // Integer sums are exact, so the split over waves and the order of the adds
@@ -35,7 +36,7 @@ namespace bl {
 
 constexpr int kBT = 512;       // threads per workgroup (8 waves)
 constexpr int kBW = kBT / 64;  // waves per workgroup
-constexpr int kBMaxTok = 16;   // one 16-token MFMA block
+constexpr int kBMaxTok = 32;   // two 16-token MFMA blocks (the second: pre-quantized rows only)
 constexpr int kBMaxRows = 32;  // at most two 16-row blocks per workgroup
 constexpr int kBMaxK = 8192;
 
@@ -105,10 +106,11 @@ __device__ inline int row16_sum(int v)
 // RB: 16-row blocks per workgroup (1 or 2). JM: quads per wave. SL: activation
 // groups of 16 inputs per thread (covering all m * k / 16 of them), or with
 // PREQ 16-byte words of the quantized rows (all m * kp / 16 of them).
-template <typename T, int RB, int JM, int SL, bool PREQ>
+template <typename T, int RB, int JM, int SL, bool PREQ, int MB>
 __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 {
-    extern __shared__ __align__(16) int8_t lds[];  // q [m][kp + 16], then partial sums [kBW][4][64]
+    static_assert(PREQ || MB == 1, "the fused quantization handles one token block");
+    extern __shared__ __align__(16) int8_t lds[];  // q [m][kp + 16], then partial sums [kBW][MB][4][64]
     __shared__ unsigned tok_max[kBMaxTok];
     __shared__ int tok_sum[kBMaxTok];
     __shared__ float tok_inv[kBMaxTok], tok_s[kBMaxTok];
@@ -246,38 +248,46 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     // 5. products: per quad, four MFMAs (dword s of each lane's 16 packed bytes
     //    against the qperm bytes of token lr at the same inputs); tokens past m
     //    and chunks past the row contribute zero
-    v4i acc = v4i{0, 0, 0, 0};
-    const int lt = lr < M ? lr : 0;
+    //    (with two token blocks each expanded operand feeds two MFMAs)
+    v4i acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
         const int cq = wave / RB + (kBW / RB) * j;
         if (cq < nq) {  // uniform
             const int c = 4 * cq + lh;
-            const bool ok = c < C && lr < M;
             const int cc = c < C ? c : C - 1;
-            const int8_t *qrow = q_lds + lt * QS + cc * 64;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const v4i qv = *reinterpret_cast<const v4i *>(qrow + s * 16);
-                const v4i bq = ok ? qv : v4i{0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(bg_expand4(wv[j][s]), bq, acc, 0, 0, 0);
+                const v4i av = bg_expand4(wv[j][s]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int t = 16 * mb + lr;
+                    const v4i qv = *reinterpret_cast<const v4i *>(q_lds + (t < M ? t : 0) * QS + cc * 64 + s * 16);
+                    const v4i bq = c < C && t < M ? qv : v4i{0, 0, 0, 0};
+                    acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq, acc[mb], 0, 0, 0);
+                }
             }
         }
     }
-    // C[row][token]: lane (h, r) holds rows 4h + v (v = 0..3) of token r
+    // C[row][token]: lane (h, r) holds rows 4h + v (v = 0..3) of token 16*mb + r
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[(wave * 4 + v) * 64 + lane] = acc[v];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[((wave * MB + mb) * 4 + v) * 64 + lane] = acc[mb][v];
     __syncthreads();
 
-    // 6. epilogue: thread -> (row block, register v, lane), summed over the
-    //    waves of its row block
-    if (tid < RB * 256) {
-        const int eb = tid >> 8, v = (tid >> 6) & 3, el = tid & 63;
-        const int row = 16 * eb + 4 * (el >> 4) + v, t = el & 15;
+    // 6. epilogue: item -> (row block, token block, register v, lane), summed
+    //    over the waves of its row block
+    for (int e = tid; e < RB * MB * 256; e += kBT) {
+        const int eb = e / (MB * 256), rem = e - eb * (MB * 256);
+        const int mb = rem >> 8, v = (rem >> 6) & 3, el = rem & 63;
+        const int row = 16 * eb + 4 * (el >> 4) + v, t = 16 * mb + (el & 15);
         if (row < rows && t < M) {
             int va = -tok_sum[t];
 #pragma unroll
-            for (int w = eb; w < kBW; w += RB) va += part[(w * 4 + v) * 64 + el];
+            for (int w = eb; w < kBW; w += RB) va += part[((w * MB + mb) * 4 + v) * 64 + el];
             const int64_t o = (int64_t)t * a.n + r0 + row;
             a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0]);
             if (a.acc_out) a.acc_out[o] = va;
@@ -289,22 +299,27 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 
 static int bgemv_slots(int64_t words) { return (int)ceil_div(words, (int64_t)kBT); }
 
+constexpr size_t kBLdsMax = 150 * 1024;
+static size_t bgemv_lds(int64_t m, int64_t kp) { return (size_t)m * (kp + 16) + (size_t)kBW * (m > 16 ? 2 : 1) * 4 * 64 * 4; }
+
 int bgemv_mode(int64_t m, int64_t k, bool bf16)
 {
     if (m < 5 || m > kBMaxTok || k > kBMaxK) return 0;
-    // fused: whole 16-input groups, at least 64 of them per token (a wave's
-    // groups touch two tokens at most) and few enough inputs that every
-    // workgroup may quantize them all
-    if (k % 16 == 0 && k >= 1024 && m * k <= 32768 && bgemv_slots(m * k / 16) <= (bf16 ? 8 : 4)) return 1;
-    return bgemv_slots(m * round_up(k, 64) / 16) <= 8 ? 2 : 0;
+    // fused: one token block, whole 16-input groups, at least 64 of them per
+    // token (a wave's groups touch two tokens at most) and few enough inputs
+    // that every workgroup may quantize them all
+    if (m <= 16 && k % 16 == 0 && k >= 1024 && m * k <= 32768 && bgemv_slots(m * k / 16) <= (bf16 ? 8 : 4))
+        return 1;
+    const int64_t kp = round_up(k, 64);
+    return bgemv_slots(m * kp / 16) <= 16 && bgemv_lds(m, kp) <= kBLdsMax ? 2 : 0;
 }
 
 namespace {
 
-template <typename T, int RB, int JM, int SL, bool PREQ>
+template <typename T, int RB, int JM, int SL, bool PREQ, int MB>
 hipError_t bg_launch(dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
 {
-    auto kern = bgemv_kernel<T, RB, JM, SL, PREQ>;
+    auto kern = bgemv_kernel<T, RB, JM, SL, PREQ, MB>;
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
         return e;
@@ -312,21 +327,27 @@ hipError_t bg_launch(dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
     return hipGetLastError();
 }
 
-template <typename T, int RB, int SL, bool PREQ>
+template <typename T, int RB, int SL, bool PREQ, int MB>
 hipError_t bg_jm(int jm, dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
 {
-    if (jm <= 1) return bg_launch<T, RB, 1, SL, PREQ>(grid, lds, st, a);
-    if (jm <= 2) return bg_launch<T, RB, 2, SL, PREQ>(grid, lds, st, a);
-    if (jm <= 3) return bg_launch<T, RB, 3, SL, PREQ>(grid, lds, st, a);
-    if (jm <= 4) return bg_launch<T, RB, 4, SL, PREQ>(grid, lds, st, a);
-    if (jm <= 6) return bg_launch<T, RB, 6, SL, PREQ>(grid, lds, st, a);
-    return bg_launch<T, RB, 8, SL, PREQ>(grid, lds, st, a);
+    if (jm <= 1) return bg_launch<T, RB, 1, SL, PREQ, MB>(grid, lds, st, a);
+    if (jm <= 2) return bg_launch<T, RB, 2, SL, PREQ, MB>(grid, lds, st, a);
+    if (jm <= 3) return bg_launch<T, RB, 3, SL, PREQ, MB>(grid, lds, st, a);
+    if (jm <= 4) return bg_launch<T, RB, 4, SL, PREQ, MB>(grid, lds, st, a);
+    if (jm <= 6) return bg_launch<T, RB, 6, SL, PREQ, MB>(grid, lds, st, a);
+    return bg_launch<T, RB, 8, SL, PREQ, MB>(grid, lds, st, a);
 }
 
-template <typename T, int SL, bool PREQ>
+template <typename T, int SL, bool PREQ, int MB = 1>
 hipError_t bg_rb(int rb, int jm, dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
 {
-    return rb == 1 ? bg_jm<T, 1, SL, PREQ>(jm, grid, lds, st, a) : bg_jm<T, 2, SL, PREQ>(jm, grid, lds, st, a);
+    return rb == 1 ? bg_jm<T, 1, SL, PREQ, MB>(jm, grid, lds, st, a) : bg_jm<T, 2, SL, PREQ, MB>(jm, grid, lds, st, a);
+}
+
+template <int SL>
+hipError_t bg_preq(int mb, int rb, int jm, dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
+{
+    return mb == 1 ? bg_rb<int8_t, SL, true, 1>(rb, jm, grid, lds, st, a) : bg_rb<int8_t, SL, true, 2>(rb, jm, grid, lds, st, a);
 }
 
 }  // namespace
@@ -347,12 +368,14 @@ hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
     const int64_t nq = ceil_div((int64_t)a.chunks, (int64_t)4);
     const int jm = (int)ceil_div(nq, (int64_t)(kBW / rb));  // <= 8: kp <= 8192
     const dim3 grid((unsigned)ceil_div(p.n, r));
-    const size_t lds = (size_t)p.m * (p.kp + 16) + (size_t)kBW * 4 * 64 * 4;
+    const size_t lds = bgemv_lds(p.m, p.kp);
     if (preq) {
+        const int mb = p.m > 16 ? 2 : 1;
         const int sl = bgemv_slots(p.m * p.kp / 16);
-        if (sl <= 2) return bg_rb<int8_t, 2, true>(rb, jm, grid, lds, st, a);
-        if (sl <= 4) return bg_rb<int8_t, 4, true>(rb, jm, grid, lds, st, a);
-        return bg_rb<int8_t, 8, true>(rb, jm, grid, lds, st, a);
+        if (sl <= 2) return bg_preq<2>(mb, rb, jm, grid, lds, st, a);
+        if (sl <= 4) return bg_preq<4>(mb, rb, jm, grid, lds, st, a);
+        if (sl <= 8) return bg_preq<8>(mb, rb, jm, grid, lds, st, a);
+        return bg_preq<16>(mb, rb, jm, grid, lds, st, a);
     }
     const int sl = bgemv_slots(p.m * p.k / 16);
     if (p.bf16) {

@@ -87,6 +87,8 @@ FWD_SHAPES = [
     (5, 256, 256), (17, 260, 33), (33, 512, 257), (64, 2560, 512), (65, 256, 300),  # MFMA paths
     (130, 640, 200), (300, 256, 130),
     (1, 256, 40000), (2, 512, 20000),  # decode: more than 64 rows per workgroup, one 8-chunk block per row
+    (12, 1024, 4000), (16, 2048, 300),   # 5..16 tokens, quantized inside the launch (k >= 1024, m*k <= 32768)
+    (20, 1000, 3000), (24, 2560, 700), (32, 4096, 300),  # 17..32 tokens: two token blocks, quantized rows
 ]
 
 
