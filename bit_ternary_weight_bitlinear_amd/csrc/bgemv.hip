@@ -36,7 +36,8 @@ namespace bl {
 
 constexpr int kBT = 512;       // threads per workgroup (8 waves)
 constexpr int kBW = kBT / 64;  // waves per workgroup
-constexpr int kBMaxTok = 32;   // two 16-token MFMA blocks (the second: pre-quantized rows only)
+constexpr int kBMaxTok = 32;   // tokens per pass: two 16-token MFMA blocks (the second: pre-quantized rows only)
+constexpr int kBMaxTokens = 64;  // tokens per launch (passes of 16 or 32)
 constexpr int kBMaxRows = 32;  // at most two 16-row blocks per workgroup
 constexpr int kBMaxK = 8192;
 
@@ -118,42 +119,50 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lh = lane >> 4;
     const int M = (int)a.m;
+    // tokens go through LDS in passes of TP (one pass unless PREQ); the weights
+    // stay in registers across the passes
+    constexpr int TP = 16 * MB;
+    const int P = PREQ ? (M + TP - 1) / TP : 1;
     const int R = a.rows_per_wg, C = a.chunks;
     const int QS = (int)a.kp + 16;  // LDS bytes per token row
     int8_t *q_lds = lds;
-    int *part = reinterpret_cast<int *>(lds + M * QS);
+    int *part = reinterpret_cast<int *>(lds + (PREQ ? min(M, TP) : M) * QS);
     const int64_t r0 = (int64_t)blockIdx.x * R;
     const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
     const T *x = static_cast<const T *>(a.x);
     const int GP = (int)(a.kp / 16);
     const int G = PREQ ? GP : (int)(a.k / 16);  // fused: k % 16 == 0
-    const int NG = M * G;
 
     if (tid < kBMaxTok) {
         tok_max[tid] = 0u;
         tok_sum[tid] = 0;
     }
 
-    // 1. activation loads (raw words); slots no thread needs are not loaded
-    //    (the condition is uniform)
+    // 1. activation loads of a pass (raw words; with PREQ the quantized rows'
+    //    16-byte words); slots no thread needs are not loaded (uniform)
     constexpr int XQ = PREQ ? 1 : (int)sizeof(T);  // 16-byte words per group
     uint4 xq[SL][XQ];
     int slot_t[SL], slot_g[SL];
+    auto load_pass = [&](int t0, int mp) {
+        const int ng = mp * G;
 #pragma unroll
-    for (int s = 0; s < SL; ++s) {
-        const int f = min(tid + s * kBT, NG - 1);
-        slot_t[s] = f / G;
-        slot_g[s] = f - slot_t[s] * G;
-        if (s * kBT < NG) {
-            const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) + (int64_t)slot_t[s] * a.kp + 16 * (int64_t)slot_g[s])
-                                  : reinterpret_cast<const uint4 *>(x + (int64_t)slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
+        for (int s = 0; s < SL; ++s) {
+            const int f = min(tid + s * kBT, ng - 1);
+            slot_t[s] = f / G;
+            slot_g[s] = f - slot_t[s] * G;
+            if (s * kBT < ng) {
+                const int64_t t = t0 + slot_t[s];
+                const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) + t * a.kp + 16 * (int64_t)slot_g[s])
+                                      : reinterpret_cast<const uint4 *>(x + t * a.k + 16 * (int64_t)slot_g[s]);
 #pragma unroll
-            for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
-        } else {
+                for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
+            } else {
 #pragma unroll
-            for (int q = 0; q < XQ; ++q) xq[s][q] = make_uint4(0, 0, 0, 0);
+                for (int q = 0; q < XQ; ++q) xq[s][q] = make_uint4(0, 0, 0, 0);
+            }
         }
-    }
+    };
+    load_pass(0, min(M, TP));  // the first pass's before the weights
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weight quads of this wave: quad wave / RB + (kBW / RB) * j of row block
@@ -172,11 +181,14 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    for (int pass = 0; pass < P; ++pass) {
+    const int t0 = pass * TP, Mp = min(TP, M - t0), NG = Mp * G;
+    if (pass > 0) load_pass(t0, Mp);
     if constexpr (PREQ) {
-        // 3-4. the quantized rows into LDS, their scales and sums
-        if (tid < M) {
-            tok_s[tid] = a.pre_s[tid];
-            tok_sum[tid] = a.pre_sumq[tid];
+        // 3-4. this pass's quantized rows into LDS, their scales and sums
+        if (tid < Mp) {
+            tok_s[tid] = a.pre_s[t0 + tid];
+            tok_sum[tid] = a.pre_sumq[t0 + tid];
         }
 #pragma unroll
         for (int s = 0; s < SL; ++s)
@@ -199,16 +211,16 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xr[j]));
         const bool valid = tid + s * kBT < NG;
-        const int t0 = f0 / G;
-        const float m0 = row16_max(valid && slot_t[s] == t0 ? mx : 0.0f);
-        const float m1 = row16_max(valid && slot_t[s] != t0 ? mx : 0.0f);
+        const int u0 = f0 / G;
+        const float m0 = row16_max(valid && slot_t[s] == u0 ? mx : 0.0f);
+        const float m1 = row16_max(valid && slot_t[s] != u0 ? mx : 0.0f);
         if (lr == 0) {
-            atomicMax(&tok_max[t0], __float_as_uint(m0));
-            if (t0 + 1 < M) atomicMax(&tok_max[t0 + 1], __float_as_uint(m1));
+            atomicMax(&tok_max[u0], __float_as_uint(m0));
+            if (u0 + 1 < Mp) atomicMax(&tok_max[u0 + 1], __float_as_uint(m1));
         }
     }
     __syncthreads();
-    if (tid < M) {
+    if (tid < Mp) {
         const float st = fmaxf(__uint_as_float(tok_max[tid]), kEps);
         tok_s[tid] = st;
         tok_inv[tid] = 127.0f / st;
@@ -230,15 +242,15 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
             sum = quant_group(xr, tok_inv[slot_t[s]], &pv, nullptr);
             *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = pv;
         }
-        const int t0 = f0 / G;
-        const int s0 = row16_sum(valid && slot_t[s] == t0 ? sum : 0);
-        const int s1 = row16_sum(valid && slot_t[s] != t0 ? sum : 0);
+        const int u0 = f0 / G;
+        const int s0 = row16_sum(valid && slot_t[s] == u0 ? sum : 0);
+        const int s1 = row16_sum(valid && slot_t[s] != u0 ? sum : 0);
         if (lr == 0) {
-            atomicAdd(&tok_sum[t0], s0);
-            if (t0 + 1 < M) atomicAdd(&tok_sum[t0 + 1], s1);
+            atomicAdd(&tok_sum[u0], s0);
+            if (u0 + 1 < Mp) atomicAdd(&tok_sum[u0 + 1], s1);
         }
     }
-    for (int i = tid; i < M * (GP - G); i += kBT) {
+    for (int i = tid; i < Mp * (GP - G); i += kBT) {
         const int t = i / (GP - G), g = G + (i - t * (GP - G));
         *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
     }
@@ -246,9 +258,9 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     }
 
     // 5. products: per quad, four MFMAs (dword s of each lane's 16 packed bytes
-    //    against the qperm bytes of token lr at the same inputs); tokens past m
-    //    and chunks past the row contribute zero
-    //    (with two token blocks each expanded operand feeds two MFMAs)
+    //    against the qperm bytes of token lr at the same inputs); tokens past
+    //    the pass and chunks past the row contribute zero (with two token
+    //    blocks each expanded operand feeds two MFMAs)
     v4i acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
@@ -264,8 +276,8 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const int t = 16 * mb + lr;
-                    const v4i qv = *reinterpret_cast<const v4i *>(q_lds + (t < M ? t : 0) * QS + cc * 64 + s * 16);
-                    const v4i bq = c < C && t < M ? qv : v4i{0, 0, 0, 0};
+                    const v4i qv = *reinterpret_cast<const v4i *>(q_lds + (t < Mp ? t : 0) * QS + cc * 64 + s * 16);
+                    const v4i bq = c < C && t < Mp ? qv : v4i{0, 0, 0, 0};
                     acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq, acc[mb], 0, 0, 0);
                 }
             }
@@ -284,14 +296,16 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         const int eb = e / (MB * 256), rem = e - eb * (MB * 256);
         const int mb = rem >> 8, v = (rem >> 6) & 3, el = rem & 63;
         const int row = 16 * eb + 4 * (el >> 4) + v, t = 16 * mb + (el & 15);
-        if (row < rows && t < M) {
+        if (row < rows && t < Mp) {
             int va = -tok_sum[t];
 #pragma unroll
             for (int w = eb; w < kBW; w += RB) va += part[((w * MB + mb) * 4 + v) * 64 + el];
-            const int64_t o = (int64_t)t * a.n + r0 + row;
+            const int64_t o = (int64_t)(t0 + t) * a.n + r0 + row;
             a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0]);
             if (a.acc_out) a.acc_out[o] = va;
         }
+    }
+    if (pass + 1 < P) __syncthreads();  // LDS rows, sums and scales are rewritten next pass
     }
 }
 
@@ -300,18 +314,28 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 static int bgemv_slots(int64_t words) { return (int)ceil_div(words, (int64_t)kBT); }
 
 constexpr size_t kBLdsMax = 150 * 1024;
-static size_t bgemv_lds(int64_t m, int64_t kp) { return (size_t)m * (kp + 16) + (size_t)kBW * (m > 16 ? 2 : 1) * 4 * 64 * 4; }
+// token blocks per pass: two when 32 token rows fit the LDS
+static int bgemv_mb(int64_t m, int64_t kp)
+{
+    return m > 16 && (size_t)32 * (kp + 16) + (size_t)kBW * 2 * 4 * 64 * 4 <= kBLdsMax ? 2 : 1;
+}
+static size_t bgemv_lds(int64_t m, int64_t kp, int mb)
+{
+    const int64_t rows = m < 16 * mb ? m : 16 * mb;
+    return (size_t)rows * (kp + 16) + (size_t)kBW * mb * 4 * 64 * 4;
+}
 
 int bgemv_mode(int64_t m, int64_t k, bool bf16)
 {
-    if (m < 5 || m > kBMaxTok || k > kBMaxK) return 0;
+    if (m < 5 || m > kBMaxTokens || k > kBMaxK) return 0;
     // fused: one token block, whole 16-input groups, at least 64 of them per
     // token (a wave's groups touch two tokens at most) and few enough inputs
     // that every workgroup may quantize them all
     if (m <= 16 && k % 16 == 0 && k >= 1024 && m * k <= 32768 && bgemv_slots(m * k / 16) <= (bf16 ? 8 : 4))
         return 1;
     const int64_t kp = round_up(k, 64);
-    return bgemv_slots(m * kp / 16) <= 16 && bgemv_lds(m, kp) <= kBLdsMax ? 2 : 0;
+    const int mb = bgemv_mb(m, kp);
+    return bgemv_slots(16 * mb * kp / 16) <= 16 && bgemv_lds(m, kp, mb) <= kBLdsMax ? 2 : 0;
 }
 
 namespace {
@@ -368,15 +392,16 @@ hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
     const int64_t nq = ceil_div((int64_t)a.chunks, (int64_t)4);
     const int jm = (int)ceil_div(nq, (int64_t)(kBW / rb));  // <= 8: kp <= 8192
     const dim3 grid((unsigned)ceil_div(p.n, r));
-    const size_t lds = bgemv_lds(p.m, p.kp);
     if (preq) {
-        const int mb = p.m > 16 ? 2 : 1;
-        const int sl = bgemv_slots(p.m * p.kp / 16);
+        const int mb = bgemv_mb(p.m, p.kp);
+        const size_t lds = bgemv_lds(p.m, p.kp, mb);
+        const int sl = bgemv_slots((p.m < 16 * mb ? p.m : 16 * mb) * p.kp / 16);
         if (sl <= 2) return bg_preq<2>(mb, rb, jm, grid, lds, st, a);
         if (sl <= 4) return bg_preq<4>(mb, rb, jm, grid, lds, st, a);
         if (sl <= 8) return bg_preq<8>(mb, rb, jm, grid, lds, st, a);
         return bg_preq<16>(mb, rb, jm, grid, lds, st, a);
     }
+    const size_t lds = bgemv_lds(p.m, p.kp, 1);
     const int sl = bgemv_slots(p.m * p.k / 16);
     if (p.bf16) {
         if (sl <= 2) return bg_rb<bf16_t, 2, false>(rb, jm, grid, lds, st, a);

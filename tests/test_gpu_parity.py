@@ -89,6 +89,7 @@ FWD_SHAPES = [
     (1, 256, 40000), (2, 512, 20000),  # decode: more than 64 rows per workgroup, one 8-chunk block per row
     (12, 1024, 4000), (16, 2048, 300),   # 5..16 tokens, quantized inside the launch (k >= 1024, m*k <= 32768)
     (20, 1000, 3000), (24, 2560, 700), (32, 4096, 300),  # 17..32 tokens: two token blocks, quantized rows
+    (40, 2560, 700), (48, 1024, 1000), (64, 6912, 300), (50, 8192, 33),  # 33..64: several token passes
 ]
 
 
