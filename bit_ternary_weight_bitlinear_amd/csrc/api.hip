@@ -212,7 +212,7 @@ bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k, cons
         return hip_status(launch_bgemv(bp, st));
     if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, k, L.kp, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
-    if (bmode == 2) {  // 5..32 tokens, quantized rows from the kernel above
+    if (bmode == 2) {  // 5..64 tokens, quantized rows from the kernel above
         bp.x = L.qp; bp.pre_s = L.s; bp.pre_sumq = L.sumq;
         return hip_status(launch_bgemv(bp, st));
     }

@@ -1,4 +1,4 @@
-// bgemv.hip -- BitLinear for 5..32 tokens (batched decode) on gfx950.
+// bgemv.hip -- BitLinear for 5..64 tokens (batched decode) on gfx950.
 //
 // The W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端) at a few
 // tokens is still a stream over the packed weights. This kernel keeps the
@@ -13,8 +13,8 @@
 //    of chunk 4*quad + h of row 16*block + r (rows past R re-read row R-1, so
 //    the request merges with a valid lane's) and feeds dword s of it, expanded
 //    in registers, as operand A of v_mfma_i32_16x16x64_i8 step s; operand B is
-//    the 16 qperm bytes of token r (of each 16-token block: 17..32 tokens run
-//    two MFMAs per operand) at the same inputs, read from LDS;
+//    the 16 qperm bytes of token r (of each 16-token block: passes of 32
+//    tokens run two MFMAs per operand) at the same inputs, read from LDS;
 //  * for m*k up to 32768 the m tokens are quantized once per workgroup, from
 //    raw words loaded before the weights and converted after the weight loads
 //    are issued: a per-token absmax (16-lane DPP maxima over the at most two
@@ -22,9 +22,10 @@
 //    token, then codes into LDS in qperm order (rows of kp + 16 bytes: the 16
 //    rows of one read phase fall on different banks) and sum_k q per token.
 //    Larger m*k would cost every workgroup too much arithmetic (2 us of VALU
-//    per CU at 8 x 6912 inputs); there, and for 17..32 tokens, the
-//    quantization kernel runs first and this one copies its int8 rows, scales
-//    and sums into LDS instead (PREQ);
+//    per CU at 8 x 6912 inputs); there, and above 16 tokens, the quantization
+//    kernel runs first and this one copies its int8 rows, scales and sums into
+//    LDS instead (PREQ), in passes of 32 tokens (when 32 rows fit the LDS) or
+//    16, while the weights stay in registers;
 //  * the waves' partial 16x16 blocks meet in LDS; the epilogue subtracts
 //    sum_k q, rescales, stores y (and the int32 sums if asked).
 // Integer sums are exact, so the split over waves and the order of the adds

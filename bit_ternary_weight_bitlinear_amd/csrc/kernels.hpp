@@ -38,12 +38,12 @@ struct GemvProblem {
     int32_t *acc_out;        // optional (single matrix only)
     int8_t *q_out;           // optional natural int8 copy of the quantized activations
     float *s_out;            // optional per-token scales
-    const float *pre_s;      // 5..32-token kernel, mode 2 only (see bgemv_mode)
+    const float *pre_s;      // 5..64-token kernel, mode 2 only (see bgemv_mode)
     const int32_t *pre_sumq;
 };
 bool gemv_supported(int64_t m, int64_t kp);
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
-// 5..32 tokens, single matrix, k <= 8192. Mode 1 (up to 16 tokens):
+// 5..64 tokens, single matrix, k <= 8192. Mode 1 (up to 16 tokens):
 // quantization inside the launch; mode 2: x holds the qperm int8 rows
 // [m][kp] of the quantization kernel and pre_s / pre_sumq its scales and
 // sums; 0: neither (too many inputs for registers or LDS).
