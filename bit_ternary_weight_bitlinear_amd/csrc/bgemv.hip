@@ -19,8 +19,9 @@
 //    raw words loaded before the weights and converted after the weight loads
 //    are issued: a per-token absmax (16-lane DPP maxima over the at most two
 //    tokens a wave's 64 groups touch, merged by LDS atomics), one division per
-//    token, then codes into LDS in qperm order (rows of kp + 16 bytes: the 16
-//    rows of one read phase fall on different banks) and sum_k q per token.
+//    token, then codes into LDS in qperm order (rows of whole chunk quads,
+//    zero past k, plus 16 bytes: the 16 rows of one read phase fall on
+//    different banks) and sum_k q per token.
 //    Larger m*k would cost every workgroup too much arithmetic (2 us of VALU
 //    per CU at 8 x 6912 inputs); there, and above 16 tokens, the quantization
 //    kernel runs first and this one copies its int8 rows, scales and sums into
@@ -125,9 +126,15 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     constexpr int TP = 16 * MB;
     const int P = PREQ ? (M + TP - 1) / TP : 1;
     const int R = a.rows_per_wg, C = a.chunks;
-    const int QS = (int)a.kp + 16;  // LDS bytes per token row
+    // LDS token rows: TP of them, each 16 * GQ bytes of qperm codes (whole
+    // quads of chunks; codes past kp and rows past the pass's tokens are zero,
+    // so the products read their operands without selects) plus 16 bytes, so
+    // the 16 rows of one read phase fall on different banks
+    const int nq = (C + 3) >> 2;
+    const int GQ = 16 * nq;
+    const int QS = 16 * GQ + 16;
     int8_t *q_lds = lds;
-    int *part = reinterpret_cast<int *>(lds + (PREQ ? min(M, TP) : M) * QS);
+    int *part = reinterpret_cast<int *>(lds + TP * QS);
     const int64_t r0 = (int64_t)blockIdx.x * R;
     const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
     const T *x = static_cast<const T *>(a.x);
@@ -163,13 +170,13 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
             }
         }
     };
-    load_pass(0, min(M, TP));  // the first pass's before the weights
+    const int Mp0 = min(M, TP);
+    load_pass(0, Mp0);  // the first pass's before the weights
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weight quads of this wave: quad wave / RB + (kBW / RB) * j of row block
     //    wave % RB; slots past the last quad re-read the last one (dropped)
     const int rb = wave % RB;
-    const int nq = (C + 3) >> 2;
     const int rr = min(16 * rb + lr, rows - 1);
     const uint8_t *wrow = a.w + (r0 + rr) * a.ldw;
     v4u wv[JM];
@@ -182,20 +189,48 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    for (int pass = 0; pass < P; ++pass) {
-    const int t0 = pass * TP, Mp = min(TP, M - t0), NG = Mp * G;
-    if (pass > 0) load_pass(t0, Mp);
-    if constexpr (PREQ) {
-        // 3-4. this pass's quantized rows into LDS, their scales and sums
-        if (tid < Mp) {
+    // zero codes: each row's groups G .. GQ, and the rows past the first
+    // pass's tokens
+    for (int i = tid; i < Mp0 * (GQ - G); i += kBT) {
+        const int t = i / (GQ - G), g = G + (i - t * (GQ - G));
+        *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
+    }
+    for (int i = tid; i < (TP - Mp0) * GQ; i += kBT) {
+        const int t = Mp0 + i / GQ, g = i - (t - Mp0) * GQ;
+        *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
+    }
+    // PREQ: a pass's quantized rows into LDS, with their scales and sums
+    auto store_pass = [&](int t0, int mp) {
+        if (tid < mp) {
             tok_s[tid] = a.pre_s[t0 + tid];
             tok_sum[tid] = a.pre_sumq[t0 + tid];
         }
+        const int ng = mp * G;
 #pragma unroll
         for (int s = 0; s < SL; ++s)
-            if (tid + s * kBT < NG)
+            if (tid + s * kBT < ng)
                 *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = xq[s][0];
+    };
+    if constexpr (PREQ) {
+        // the first pass outside the loop: it waits for its rows only, not
+        // for the weights requested after them
+        store_pass(0, Mp0);
         __syncthreads();
+    }
+
+    for (int pass = 0; pass < P; ++pass) {
+    const int t0 = pass * TP, Mp = min(TP, M - t0), NG = Mp * G;
+    if constexpr (PREQ) {
+        if (pass > 0) {
+            load_pass(t0, Mp);
+            store_pass(t0, Mp);
+            // a short last pass: its rows past the tokens read as zero
+            for (int i = tid; i < (TP - Mp) * G; i += kBT) {
+                const int t = Mp + i / G, g = i - (t - Mp) * G;
+                *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
+            }
+            __syncthreads();
+        }
     } else {
     // 3. per-token absmax. The 64 groups of one wave and slot belong to at most
     //    two tokens (t0 and t0 + 1: a token has G >= 64 groups); each 16-lane
@@ -228,8 +263,8 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     }
     __syncthreads();
 
-    // 4. codes into LDS (qperm order) and sum_k q per token; padding inputs of
-    //    each token row (k .. kp) are zero
+    // 4. codes into LDS (qperm order) and sum_k q per token (inputs past k
+    //    were zeroed above)
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
         const int f0 = wave * 64 + s * kBT;
@@ -251,16 +286,12 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
             if (u0 + 1 < Mp) atomicAdd(&tok_sum[u0 + 1], s1);
         }
     }
-    for (int i = tid; i < Mp * (GP - G); i += kBT) {
-        const int t = i / (GP - G), g = G + (i - t * (GP - G));
-        *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
-    }
     __syncthreads();
     }
 
     // 5. products: per quad, four MFMAs (dword s of each lane's 16 packed bytes
     //    against the qperm bytes of token lr at the same inputs); tokens past
-    //    the pass and chunks past the row contribute zero (with two token
+    //    the pass and chunks past the row read zero codes (with two token
     //    blocks each expanded operand feeds two MFMAs)
     v4i acc[MB];
 #pragma unroll
@@ -269,18 +300,14 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     for (int j = 0; j < JM; ++j) {
         const int cq = wave / RB + (kBW / RB) * j;
         if (cq < nq) {  // uniform
-            const int c = 4 * cq + lh;
-            const int cc = c < C ? c : C - 1;
+            const int8_t *qc = q_lds + lr * QS + (4 * cq + lh) * 64;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const v4i av = bg_expand4(wv[j][s]);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int t = 16 * mb + lr;
-                    const v4i qv = *reinterpret_cast<const v4i *>(q_lds + (t < Mp ? t : 0) * QS + cc * 64 + s * 16);
-                    const v4i bq = c < C && t < Mp ? qv : v4i{0, 0, 0, 0};
-                    acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq, acc[mb], 0, 0, 0);
-                }
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        av, *reinterpret_cast<const v4i *>(qc + 16 * mb * QS + s * 16), acc[mb], 0, 0, 0);
             }
         }
     }
@@ -316,14 +343,15 @@ static int bgemv_slots(int64_t words) { return (int)ceil_div(words, (int64_t)kBT
 
 constexpr size_t kBLdsMax = 150 * 1024;
 // token blocks per pass: two when 32 token rows fit the LDS
+// LDS bytes: 16 * mb token rows of whole chunk quads plus 16 bytes, then the
+// waves' partial sums
+static size_t bgemv_lds(int64_t kp, int mb)
+{
+    return (size_t)16 * mb * (round_up(kp, 256) + 16) + (size_t)kBW * mb * 4 * 64 * 4;
+}
 static int bgemv_mb(int64_t m, int64_t kp)
 {
-    return m > 16 && (size_t)32 * (kp + 16) + (size_t)kBW * 2 * 4 * 64 * 4 <= kBLdsMax ? 2 : 1;
-}
-static size_t bgemv_lds(int64_t m, int64_t kp, int mb)
-{
-    const int64_t rows = m < 16 * mb ? m : 16 * mb;
-    return (size_t)rows * (kp + 16) + (size_t)kBW * mb * 4 * 64 * 4;
+    return m > 16 && bgemv_lds(kp, 2) <= kBLdsMax ? 2 : 1;
 }
 
 int bgemv_mode(int64_t m, int64_t k, bool bf16)
@@ -336,7 +364,7 @@ int bgemv_mode(int64_t m, int64_t k, bool bf16)
         return 1;
     const int64_t kp = round_up(k, 64);
     const int mb = bgemv_mb(m, kp);
-    return bgemv_slots(16 * mb * kp / 16) <= 16 && bgemv_lds(m, kp, mb) <= kBLdsMax ? 2 : 0;
+    return bgemv_slots(16 * mb * kp / 16) <= 16 && bgemv_lds(kp, mb) <= kBLdsMax ? 2 : 0;
 }
 
 namespace {
@@ -395,14 +423,14 @@ hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
     const dim3 grid((unsigned)ceil_div(p.n, r));
     if (preq) {
         const int mb = bgemv_mb(p.m, p.kp);
-        const size_t lds = bgemv_lds(p.m, p.kp, mb);
+        const size_t lds = bgemv_lds(p.kp, mb);
         const int sl = bgemv_slots((p.m < 16 * mb ? p.m : 16 * mb) * p.kp / 16);
         if (sl <= 2) return bg_preq<2>(mb, rb, jm, grid, lds, st, a);
         if (sl <= 4) return bg_preq<4>(mb, rb, jm, grid, lds, st, a);
         if (sl <= 8) return bg_preq<8>(mb, rb, jm, grid, lds, st, a);
         return bg_preq<16>(mb, rb, jm, grid, lds, st, a);
     }
-    const size_t lds = bgemv_lds(p.m, p.kp, 1);
+    const size_t lds = bgemv_lds(p.kp, 1);
     const int sl = bgemv_slots(p.m * p.k / 16);
     if (p.bf16) {
         if (sl <= 2) return bg_rb<bf16_t, 2, false>(rb, jm, grid, lds, st, a);
