@@ -18,9 +18,10 @@ Timing: HIP events on the stream the kernels run on. `roofline` uses the
 dominant kernel's average launch duration from per-launch event pairs.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-`--profile decode|prefill` runs the workload eagerly (no graph capture, no
-JSON line) for profilers: `--steps` steps, then one plain device copy of
-256 MiB whose HBM byte counters calibrate those of the kernels.
+`--profile decode|prefill|layer8|ffn1` runs one workload eagerly (no graph
+capture, no JSON line) for profilers: `--steps` steps, then one plain device
+copy of 256 MiB whose HBM byte counters calibrate those of the kernels.
+layer8 is the batched-decode layer at 8 tokens, ffn1 the 8B FFN at one token.
 """
 from __future__ import annotations
 
@@ -280,6 +281,33 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
             ws = pool[i % len(pool)]
             for j in range(2):
                 bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
+    elif what == "layer8":
+        # the 2B-class layer at 8 tokens, weights cold from the rotation pool
+        cfg = synth.WORKLOADS[3]
+        m = 8
+        mats = [make_weights(bl, torch, 3, tid, n, k, dev)
+                for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), cfg["mats"])]
+        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        xs = [act_tensor(torch, 3, m, k, dev) for k, _ in cfg["mats"]]
+        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
+        wss = [torch.empty(max(1, bl.workspace_size(bl.OP_FORWARD, m, k, n)), dtype=torch.uint8, device=dev)
+               for k, n in cfg["mats"]]
+        for i in range(steps):
+            ws = pool[i % len(pool)]
+            for j in range(len(mats)):
+                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j], workspace=wss[j])
+    elif what == "ffn1":
+        # the 8B-class FFN block at one token, weights cold from the rotation pool
+        cfg = synth.WORKLOADS[5]
+        hid, f = cfg["hidden"], cfg["ffn"]
+        mats = [make_weights(bl, torch, 5, "gate", f, hid, dev), make_weights(bl, torch, 5, "up", f, hid, dev),
+                make_weights(bl, torch, 5, "down", hid, f, dev)]
+        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        x = act_tensor(torch, 5, 1, hid, dev)
+        ws = torch.empty(bl.workspace_size(bl.OP_FFN, 1, hid, f), dtype=torch.uint8, device=dev)
+        for i in range(steps):
+            g, u, d = pool[i % len(pool)]
+            bl.ffn(x, g, u, d, workspace=ws)
     else:
         cfg = synth.WORKLOADS[4]
         m = cfg["m"]
@@ -335,7 +363,7 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--workload", choices=["default", "all"], default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "ffn1"], default=None,
                     help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 
