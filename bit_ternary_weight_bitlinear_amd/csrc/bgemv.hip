@@ -113,7 +113,7 @@ template <typename T, int RB, int JM, int SL, bool PREQ, int MB>
 __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 {
     static_assert(PREQ || MB == 1, "the fused quantization handles one token block");
-    extern __shared__ __align__(16) int8_t lds[];  // q [m][kp + 16], then partial sums [kBW][MB][4][64]
+    extern __shared__ __align__(16) int8_t lds[];  // token rows [TP][QS], then partial sums [kBW][MB][4][64]
     __shared__ unsigned tok_max[kBMaxTok];
     __shared__ int tok_sum[kBMaxTok];
     __shared__ float tok_inv[kBMaxTok], tok_s[kBMaxTok];
