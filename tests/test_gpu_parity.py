@@ -219,7 +219,8 @@ def test_workload_ffn_8b_prefill(bl):
 
 # ------------------------------------------------------------------ HIP graph capture
 
-@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (3, 1024, 300), (64, 2560, 512), (300, 512, 640)])
+@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (3, 1024, 300), (8, 2560, 700), (64, 2560, 512),
+                                   (300, 512, 640)])
 def test_graph_replay_matches_eager(bl, m, k, n):
     """The library enqueues only kernels (no allocation, no memset), so a captured
     forward must reproduce the eager result on every replay."""
