@@ -489,17 +489,21 @@ static hipError_t launch_fm1(const GemmArgs &a, hipStream_t st)
     return launch_tile<1, FN, EPI, 8, 1>(a, st);
 }
 
-// Tile shape: the (FM, FN) whose tile count fills the 256 CUs in the fewest
-// rounds, by a per-tile cost of FM*FN*NA MFMA blocks plus a fixed per-step
+// Tile shape: the (FM, FN) of least cost, rounds over the 256 CUs times a
+// per-tile cost of FM*FN*NA MFMA blocks, the weight expansion (about 0.2 of
+// a block per block on 128-token tiles, half that on 256-token tiles, which
+// expand each operand once for two MFMAs: the gate/up pair at 2048 x 14336
+// took 315 us on 128x192 tiles and 265 us on 256x128) and a fixed per-step
 // overhead. Shapes are limited to those whose accumulators and operands fit
 // the register file without spilling: at most 14 accumulator blocks for one
-// matrix and 12 for the gate/up pair.
+// matrix; for the gate/up pair 12 on 128-token tiles, or 256x128 (16 blocks:
+// all 256 AGPRs and 256 VGPRs).
 struct TileShape {
     int fm, fn;
 };
 static bool tile_allowed(int fm, int fn, int na)
 {
-    if (na == 2) return fm == 1 && fn <= 6;
+    if (na == 2) return (fm == 1 && fn <= 6) || (fm == 2 && fn == 4);
     return fm * fn <= 14;
 }
 static TileShape pick_tile(int64_t m, int64_t n, int na)
@@ -511,7 +515,7 @@ static TileShape pick_tile(int64_t m, int64_t n, int na)
             if (!tile_allowed(fm, fn, na)) continue;
             const int64_t tiles = ceil_div(n, 32 * fn) * ceil_div(m, 128 * fm);
             const int64_t rounds = ceil_div(tiles, 256);
-            const double cost = (double)rounds * (fm * fn * na + 3.0);
+            const double cost = (double)rounds * (fm * fn * na * (1.0 + 0.2 / fm) + 3.0);
             if (cost < best_cost) {
                 best_cost = cost;
                 best = TileShape{fm, fn};
@@ -542,6 +546,7 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
         default: return launch_fm1<8, EPI>(a, st);
         }
     } else {
+        if (t.fm == 2) return launch_tile<2, 4, EPI, 5>(a, st);  // 138 KB of LDS
         switch (t.fn) {
         case 4: return launch_tile<1, 4, EPI, 8>(a, st);
         case 5: return launch_tile<1, 5, EPI, 8>(a, st);

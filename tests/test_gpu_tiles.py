@@ -26,18 +26,19 @@ from tests.gpu_util import assert_y_close, host, make_linear, to_dev  # noqa: E4
 
 
 def pick_tile(m, n, na):
-    """Mirror of the host-side tile choice: fewest rounds over 256 CUs, then the
-    cheapest tile, among shapes with at most 14 (one matrix) or 12 (gate/up)
-    accumulator blocks."""
+    """Mirror of the host-side tile choice: least rounds over 256 CUs times the
+    per-tile cost (MFMA blocks, their weight expansion, a fixed per-step term),
+    among shapes with at most 14 (one matrix) accumulator blocks, or for the
+    gate/up pair 12 on 128-token tiles or the 256x128 tile."""
     best, best_cost = (1, 4), math.inf
     for fm in (2, 1):
         for fn in range(8, 3, -1):
-            if na == 2 and not (fm == 1 and fn <= 6):
+            if na == 2 and not ((fm == 1 and fn <= 6) or (fm == 2 and fn == 4)):
                 continue
             if na == 1 and fm * fn > 14:
                 continue
             tiles = math.ceil(n / (32 * fn)) * math.ceil(m / (128 * fm))
-            cost = math.ceil(tiles / 256) * (fm * fn * na + 3)
+            cost = math.ceil(tiles / 256) * (fm * fn * na * (1.0 + 0.2 / fm) + 3.0)
             if cost < best_cost:
                 best_cost, best = cost, (fm, fn)
     return best
@@ -59,7 +60,7 @@ def ragged_shape(fm, fn, na):
 
 
 SINGLE = [(2, 4), (2, 5), (2, 6), (2, 7), (1, 4), (1, 5), (1, 6), (1, 7), (1, 8)]
-PAIR = [(1, 4), (1, 5), (1, 6)]
+PAIR = [(1, 4), (1, 5), (1, 6), (2, 4)]
 
 
 @pytest.fixture(scope="module")
