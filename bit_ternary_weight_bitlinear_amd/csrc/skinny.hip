@@ -13,6 +13,9 @@
 //  * the four waves' partial sums meet in LDS; the epilogue subtracts
 //    sum_k q, rescales and stores.
 // All sums are exact integers, so the split over waves does not change results.
+// bitlinear_forward takes the kernel in bgemv.hip for these token counts when
+// k <= 8192; this one serves longer rows, the FFN block's contractions and the
+// integer-only entry point.
 #include "common.hpp"
 #include "kernels.hpp"
 
