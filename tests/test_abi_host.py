@@ -92,3 +92,14 @@ def test_other_entry_points_argument_errors(lib):
     assert ffn(A, 1, 1, 256, 510, A, A, A, A, A, A, A, None, None, A, 1 << 20, None) == BL_ERR_SHAPE
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, A, A, A, MIS, None, A, 1 << 20, None) == BL_ERR_ALIGN
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, A, A, A, None, None, A, 16, None) == BL_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No CPU fallback: with the shared library absent, every call raises."""
+    import bit_ternary_weight_bitlinear_amd as bl
+    monkeypatch.setattr(bl, "_lib", None)
+    monkeypatch.setattr(bl, "_LIB_PATH", str(tmp_path / "libbitlinear.so"))
+    with pytest.raises(bl.BitLinearError):
+        bl.load_library()
+    with pytest.raises(bl.BitLinearError):
+        bl.workspace_size(bl.OP_FORWARD, 1, 256, 256)
