@@ -40,24 +40,33 @@ __device__ inline int qperm_index(int k) { return (k & ~15) | ((k & 3) << 2) | (
 
 // ---------------------------------------------------------------- DPP reductions
 // Butterfly inside each 16-lane row with DPP (quad_perm xor1, quad_perm xor2,
-// row_half_mirror, row_mirror), then across the four rows with lane shuffles.
+// row_half_mirror, row_mirror), then across the four rows with DPP row
+// broadcasts.
 constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
 
 template <int CTRL>
 __device__ inline int dpp_mov(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
 
+// Across the four rows: row_bcast:15 adds lane 15 of rows 0 and 2 into rows
+// 1 and 3, row_bcast:31 lane 31 into rows 2 and 3, so lane 63 ends with the
+// whole wave's result, which v_readlane hands to every lane (no LDS permute).
+// Rows outside a step's row mask take `old`: v for max, 0 for sums.
 __device__ inline float wave_max(float v)
 {
     v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor1>(__float_as_int(v))));
     v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor2>(__float_as_int(v))));
     v = fmaxf(v, __int_as_float(dpp_mov<kDppRowHalfMirror>(__float_as_int(v))));
     v = fmaxf(v, __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v))));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    int b = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, kDppRowBcast15, 0xA, 0xF, false)));
+    b = __float_as_int(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, kDppRowBcast31, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // sum over each group of 8 lanes (8i .. 8i+7); every lane of the group gets it
@@ -75,9 +84,9 @@ __device__ inline int wave_sum(int v)
     v += dpp_mov<kDppQuadXor2>(v);
     v += dpp_mov<kDppRowHalfMirror>(v);
     v += dpp_mov<kDppRowMirror>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // ---------------------------------------------------------------- activation loads
