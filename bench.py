@@ -91,22 +91,28 @@ class Timer:
         return g
 
     def graph_region(self, fn, steps, per_graph):
-        """Replays a graph of `per_graph` steps until >= steps are done.
-        Returns (seconds per step, steps done)."""
+        """Times exactly `steps` steps: a graph of `per_graph` steps (one cycle
+        of the weight pool) replayed steps // per_graph times, then a graph of
+        the remaining steps. Returns (seconds per step, steps done)."""
         t = self.torch
-        g = self.capture(fn, per_graph)
-        reps = max(1, -(-steps // per_graph))
-        g.replay()  # warm replay
+        steps = max(1, steps)
+        reps, rest = divmod(steps, per_graph)
+        g = self.capture(fn, per_graph) if reps else None
+        g_rest = self.capture(fn, rest) if rest else None
+        for gr in (g, g_rest):  # warm replays
+            if gr is not None:
+                gr.replay()
         t.cuda.synchronize()
         st = t.cuda.current_stream()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         a.record(st)
         for _ in range(reps):
             g.replay()
+        if g_rest is not None:
+            g_rest.replay()
         b.record(st)
         t.cuda.synchronize()
-        done = reps * per_graph
-        return a.elapsed_time(b) / 1e3 / done, done
+        return a.elapsed_time(b) / 1e3 / steps, steps
 
 
 def make_weights(bl, torch, cfg, tid, n, k, dev):
