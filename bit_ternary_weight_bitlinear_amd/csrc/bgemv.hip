@@ -57,55 +57,6 @@ struct BgemvArgs {
     int chunks;       // kp / 64
 };
 
-__device__ inline v4i bg_expand4(uint32_t w)
-{
-    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-               (int)((w >> 6) & 0x03030303u)};
-}
-
-// The 16 inputs of one group from its raw 16-byte words (bf16: 2, fp32: 4).
-template <typename T>
-__device__ inline void bg_unpack(const uint4 *v, float f[16])
-{
-    if constexpr (sizeof(T) == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[4 * j + 0] = __uint_as_float(v[j].x);
-            f[4 * j + 1] = __uint_as_float(v[j].y);
-            f[4 * j + 2] = __uint_as_float(v[j].z);
-            f[4 * j + 3] = __uint_as_float(v[j].w);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
-                f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-            }
-        }
-    }
-}
-
-// maximum / sum over each row of 16 lanes (every lane of the row gets it)
-__device__ inline float row16_max(float v)
-{
-    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor1>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor2>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowHalfMirror>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v))));
-    return v;
-}
-__device__ inline int row16_sum(int v)
-{
-    v += dpp_mov<kDppQuadXor1>(v);
-    v += dpp_mov<kDppQuadXor2>(v);
-    v += dpp_mov<kDppRowHalfMirror>(v);
-    v += dpp_mov<kDppRowMirror>(v);
-    return v;
-}
-
 // RB: 16-row blocks per workgroup (1 or 2). JM: quads per wave. SL: activation
 // groups of 16 inputs per thread (covering all m * k / 16 of them), or with
 // PREQ 16-byte words of the quantized rows (all m * kp / 16 of them).
@@ -242,7 +193,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         const int f0 = wave * 64 + s * kBT;  // first group of this wave and slot
         if (f0 >= NG) continue;              // uniform
         float xr[16];
-        bg_unpack<T>(xq[s], xr);
+        unpack_group<T>(xq[s], xr);
         float mx = 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xr[j]));
@@ -273,7 +224,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         int sum = 0;
         if (valid) {
             float xr[16];
-            bg_unpack<T>(xq[s], xr);
+            unpack_group<T>(xq[s], xr);
             uint4 pv;
             sum = quant_group(xr, tok_inv[slot_t[s]], &pv, nullptr);
             *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = pv;
@@ -303,7 +254,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
             const int8_t *qc = q_lds + lr * QS + (4 * cq + lh) * 64;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const v4i av = bg_expand4(wv[j][s]);
+                const v4i av = expand_codes4(wv[j][s]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(

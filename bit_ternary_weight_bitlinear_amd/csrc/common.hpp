@@ -69,6 +69,24 @@ __device__ inline float wave_max(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// maximum / sum over each row of 16 lanes (every lane of the row gets it)
+__device__ inline float row16_max(float v)
+{
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppRowMirror>(__float_as_int(v))));
+    return v;
+}
+__device__ inline int row16_sum(int v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    v += dpp_mov<kDppRowHalfMirror>(v);
+    v += dpp_mov<kDppRowMirror>(v);
+    return v;
+}
+
 // sum over each group of 8 lanes (8i .. 8i+7); every lane of the group gets it
 __device__ inline int group8_sum(int v)
 {
@@ -186,6 +204,41 @@ __device__ inline int quant_group(const float f[16], float inv, uint4 *perm_out,
     if (perm_out) *perm_out = make_uint4(pd[0], pd[1], pd[2], pd[3]);
     if (nat_out) *nat_out = make_uint4(nd[0], nd[1], nd[2], nd[3]);
     return sum;
+}
+
+// The four 2-bit fields of a packed dword as int8 operand bytes: dword i holds
+// (w >> 2i) & 0x03030303, the codes of inputs 16g + 4b + i for bytes b = 0..3
+// of the dword covering group g -- the qperm byte order of the activations.
+__device__ inline v4i expand_codes4(uint32_t w)
+{
+    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+               (int)((w >> 6) & 0x03030303u)};
+}
+
+// The 16 inputs of one group from its raw 16-byte words (bf16: 2, fp32: 4),
+// loaded earlier so that the conversion does not hold up other requests.
+template <typename T>
+__device__ inline void unpack_group(const uint4 *v, float f[16])
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[4 * j + 0] = __uint_as_float(v[j].x);
+            f[4 * j + 1] = __uint_as_float(v[j].y);
+            f[4 * j + 2] = __uint_as_float(v[j].z);
+            f[4 * j + 3] = __uint_as_float(v[j].w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
+                f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+        }
+    }
 }
 
 // Packs 16 codes into the qperm byte order (used where codes are already ints).

@@ -51,38 +51,14 @@ struct GemvArgs {
     int chunks;       // kp / 64
 };
 
-// The 16 inputs of one group from its raw 16-byte words (bf16: 2, fp32: 4).
-template <typename T>
-__device__ inline void unpack_group(const uint4 *v, float f[16])
-{
-    if constexpr (sizeof(T) == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[4 * j + 0] = __uint_as_float(v[j].x);
-            f[4 * j + 1] = __uint_as_float(v[j].y);
-            f[4 * j + 2] = __uint_as_float(v[j].z);
-            f[4 * j + 3] = __uint_as_float(v[j].w);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[8 * j + 2 * e + 0] = __uint_as_float(w[e] << 16);
-                f[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-            }
-        }
-    }
-}
-
 // LDS slot of activation group (c, d): 16-byte slots rotated by (c >> 2) & 3 so
 // that lanes reading neighbouring chunks spread over the banks.
 __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) & 3)) << 4); }
 
 // RES: all m*ceil(k/16) activation groups fit in SL <= kSlots per thread
 // (loaded once, quantized from registers; SL is sized to the problem so that
-// unused slots hold no registers). FULL: k % 16 == 0. JM: weight tasks per thread.
+// unused slots hold no registers). FULL: k % 16 == 0. JM: (row, 8-chunk block)
+// units per lane group.
 template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
@@ -112,7 +88,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     //    and the quantization ends later (measured: ~0.3 us per launch either
     //    way). Every slot is loaded (clamped to a valid group), with no branch.
     constexpr bool kActFirst = JM * NA >= 6;
-    constexpr int XQ = (int)sizeof(T) * 16 / 16;  // 16-byte words per group
+    constexpr int XQ = (int)sizeof(T);  // 16-byte words per 16-input group (bf16: 2, fp32: 4)
     uint4 xq[SL][XQ];
     int slot_t[SL], slot_g[SL];
     if constexpr (RES) {

@@ -36,12 +36,6 @@ struct SkinnyArgs {
     int32_t *acc_out;
 };
 
-__device__ inline v4i expand_codes4(uint32_t w)
-{
-    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-               (int)((w >> 6) & 0x03030303u)};
-}
-
 // MB: 16-token blocks (1..4). EPI as for the GEMM. KB > 0: each wave has at
 // most KB blocks, all requested at the start.
 template <int MB, int EPI, int KB = 0>
