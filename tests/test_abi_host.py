@@ -69,6 +69,12 @@ def test_forward_argument_errors(lib):
     assert f(A, 0, 1, 258, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
     assert f(A, 0, 1, 0, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
     assert f(A, 0, 1, 256, A, A, 0, A, None, None, 0, None) == BL_ERR_SHAPE
+    # one past the largest accepted sizes (2^20 inputs or outputs, 2^22 tokens)
+    assert f(A, 0, 1, (1 << 20) + 4, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
+    assert f(A, 0, 1, 256, A, A, (1 << 20) + 1, A, None, None, 0, None) == BL_ERR_SHAPE
+    assert f(A, 0, (1 << 22) + 1, 256, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
+    assert lib.bitlinear_workspace_size(1, 1 << 22, 4, 3) > 0
+    assert lib.bitlinear_workspace_size(1, (1 << 22) + 1, 4, 3) == 0
     assert f(MIS, 0, 1, 256, A, A, 8, A, None, None, 0, None) == BL_ERR_ALIGN
     assert f(A, 0, 1, 256, MIS, A, 8, A, None, None, 0, None) == BL_ERR_ALIGN
     assert f(A, 0, 1, 256, A, A, 8, A, MIS, None, 0, None) == BL_ERR_ALIGN

@@ -132,6 +132,24 @@ def test_gemm_i32_bit_exact(bl):
         np.testing.assert_array_equal(host(acc), q.astype(np.int64) @ wt.astype(np.int64).T)
 
 
+# the largest sizes the boundary accepts (BL_MAX_DIM = 2^20 inputs or outputs,
+# BL_MAX_TOKENS = 2^22 tokens), each with the other dimensions small
+MAX_SHAPES = [(2, 1 << 20, 5), (1, 20, 1 << 20), (1 << 22, 4, 3)]
+
+
+@pytest.mark.parametrize("m,k,n", MAX_SHAPES)
+def test_forward_maximum_sizes(bl, m, k, n):
+    w, p_ref, g_ref, _ = make_linear(96, 1, n, k)
+    x = synth.activations(96, m, k, dtype="f32", outlier_channels=2, outlier_scale=20.0)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    assert host(gamma)[0].view(np.uint32) == np.float32(g_ref).view(np.uint32)
+    np.testing.assert_array_equal(host(packed), p_ref)
+    y, acc = bl.forward(to_dev(x), packed, gamma, return_acc=True)
+    r = oracle.forward(x, p_ref, g_ref, k, "f32")
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
+
+
 def test_forward_deterministic(bl):
     w, _, _, _ = make_linear(95, 1, 6912, 2560)
     packed, gamma = bl.pack_weights(to_dev(w))
@@ -194,7 +212,8 @@ def _ffn_case(bl, cfg, m, hid, f, sample=None, dtype="bf16"):
 
 @pytest.mark.parametrize("m,hid,f", [(1, 256, 512), (3, 260, 516), (4, 512, 1024), (5, 256, 512),
                                      (33, 260, 516), (130, 512, 768),
-                                     (1, 256, 20000)])  # gate/up pair with more than 64 rows per workgroup
+                                     (1, 256, 20000),  # gate/up pair with more than 64 rows per workgroup
+                                     (2, 8, 1 << 20)])  # the largest ffn width the boundary accepts
 def test_ffn_small(bl, m, hid, f):
     _ffn_case(bl, 96, m, hid, f)
 
