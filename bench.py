@@ -15,7 +15,8 @@ layers on the int8 MFMA path; TOPS = 2*M*N*K per layer / step time.
 8B-class FFN block (m = 1, 2048) under "extra".
 
 Timing: HIP events on the stream the kernels run on. `roofline` uses the
-dominant kernel's average launch duration from per-launch event pairs.
+dominant kernel's average launch duration: a graph of launches of that kernel
+alone (one matrix at a time, the same weight pool), timed over K launches.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
 `--profile decode|prefill|layer8|ffn1` runs one workload eagerly (no graph
