@@ -98,27 +98,37 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     }
 
     // 1. activation loads of a pass (raw words; with PREQ the quantized rows'
-    //    16-byte words); slots no thread needs are not loaded (uniform)
+    //    16-byte words); slots no thread needs are not loaded (uniform). Slot s
+    //    of a thread is the pass's flat group f = tid + s * kBT, i.e. group
+    //    f % G of token f / G; a token row is exactly G groups wide (k = 16 G,
+    //    or with PREQ rows of kp = 16 G bytes), so its address is 16 f past
+    //    the pass's first row and the division waits until the loads are out
     constexpr int XQ = PREQ ? 1 : (int)sizeof(T);  // 16-byte words per group
     uint4 xq[SL][XQ];
-    int slot_t[SL], slot_g[SL];
+    int slot_f[SL], slot_t[SL], slot_g[SL];
     auto load_pass = [&](int t0, int mp) {
         const int ng = mp * G;
+        const int64_t g0 = (int64_t)t0 * G;  // the pass's first group
 #pragma unroll
         for (int s = 0; s < SL; ++s) {
-            const int f = min(tid + s * kBT, ng - 1);
-            slot_t[s] = f / G;
-            slot_g[s] = f - slot_t[s] * G;
+            slot_f[s] = min(tid + s * kBT, ng - 1);
             if (s * kBT < ng) {
-                const int64_t t = t0 + slot_t[s];
-                const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) + t * a.kp + 16 * (int64_t)slot_g[s])
-                                      : reinterpret_cast<const uint4 *>(x + t * a.k + 16 * (int64_t)slot_g[s]);
+                const int64_t e = 16 * (g0 + slot_f[s]);  // elements (PREQ: bytes)
+                const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) + e)
+                                      : reinterpret_cast<const uint4 *>(x + e);
 #pragma unroll
                 for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
             } else {
 #pragma unroll
                 for (int q = 0; q < XQ; ++q) xq[s][q] = make_uint4(0, 0, 0, 0);
             }
+        }
+    };
+    auto split_slots = [&] {
+#pragma unroll
+        for (int s = 0; s < SL; ++s) {
+            slot_t[s] = slot_f[s] / G;
+            slot_g[s] = slot_f[s] - slot_t[s] * G;
         }
     };
     const int Mp0 = min(M, TP);
@@ -139,6 +149,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         // issue order = use order, so each quad waits only for its own load
         __builtin_amdgcn_sched_barrier(0);
     }
+    split_slots();
 
     // zero codes: each row's groups G .. GQ, and the rows past the first
     // pass's tokens
@@ -174,6 +185,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     if constexpr (PREQ) {
         if (pass > 0) {
             load_pass(t0, Mp);
+            split_slots();
             store_pass(t0, Mp);
             // a short last pass: its rows past the tokens read as zero
             for (int i = tid; i < (TP - Mp) * G; i += kBT) {
