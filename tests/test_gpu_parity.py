@@ -58,7 +58,8 @@ def test_pack_hand_worked(bl, golden):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("m,k", [(1, 4), (3, 20), (4, 256), (5, 260), (2, 2560), (3, 6912), (2, 14336),
-                                 (1, 16388), (64, 4096)])
+                                 (1, 16388), (64, 4096),
+                                 (1030, 260), (1024, 8192), (1027, 8196)])  # many tokens, ragged and whole rows
 def test_quant_act_bit_exact(bl, dtype, m, k):
     x = synth.activations(91, m, k, dtype=dtype, outlier_channels=min(3, k), outlier_scale=30.0)
     q, s = bl.quant_act(to_dev(x, dtype))
