@@ -200,11 +200,12 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     //    row reduces both with DPP and its lane 0 merges them into the tokens'
     //    maxima (integer max of non-negative float bits).
     __syncthreads();  // tok_max / tok_sum cleared
+    float xk[SL][16];  // the inputs, converted once for both passes over them
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
         const int f0 = wave * 64 + s * kBT;  // first group of this wave and slot
         if (f0 >= NG) continue;              // uniform
-        float xr[16];
+        float *xr = xk[s];
         unpack_group<T>(xq[s], xr);
         float mx = 0.0f;
 #pragma unroll
@@ -235,10 +236,8 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         const bool valid = tid + s * kBT < NG;
         int sum = 0;
         if (valid) {
-            float xr[16];
-            unpack_group<T>(xq[s], xr);
             uint4 pv;
-            sum = quant_group(xr, tok_inv[slot_t[s]], &pv, nullptr);
+            sum = quant_group(xk[s], tok_inv[slot_t[s]], &pv, nullptr);
             *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = pv;
         }
         const int u0 = f0 / G;
