@@ -18,7 +18,7 @@
  * the precision the kernels decide integers in (fp32), with the operation order
  * fixed below; the weight-scale reduction accumulates in fp64.
  *
- * Readings where the pages leave the step open (each is listed in the design doc):
+ * Readings where the pages leave the step open:
  *  - weight quantizer: absmean RoundClip with one per-tensor scale gamma [P1, P3];
  *  - ties round half to even (rintf under the default rounding mode);
  *  - gamma = 0 (all-zero weight) stores gamma = 0 and every weight quantizes to 0;
