@@ -19,10 +19,11 @@ dominant kernel's average launch duration: a graph of launches of that kernel
 alone (one matrix at a time, the same weight pool), timed over K launches.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-`--profile decode|prefill|layer8|ffn1` runs one workload eagerly (no graph
+`--profile decode|prefill|layer8|ffn1|ffn2048` runs one workload eagerly (no graph
 capture, no JSON line) for profilers: `--steps` steps, then one plain device
 copy of 256 MiB whose HBM byte counters calibrate those of the kernels.
-layer8 is the batched-decode layer at 8 tokens, ffn1 the 8B FFN at one token.
+layer8 is the batched-decode layer at 8 tokens, ffn1 / ffn2048 the 8B FFN at
+one / 2048 tokens.
 """
 from __future__ import annotations
 
@@ -315,6 +316,17 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
         for i in range(steps):
             g, u, d = pool[i % len(pool)]
             bl.ffn(x, g, u, d, workspace=ws)
+    elif what == "ffn2048":
+        # the 8B-class FFN block at 2048 tokens (compute-bound: one copy of the weights)
+        cfg = synth.WORKLOADS[5]
+        hid, f, m = cfg["hidden"], cfg["ffn"], max(cfg["ms"])
+        g = make_weights(bl, torch, 5, "gate", f, hid, dev)
+        u = make_weights(bl, torch, 5, "up", f, hid, dev)
+        d = make_weights(bl, torch, 5, "down", hid, f, dev)
+        x = act_tensor(torch, 5, m, hid, dev)
+        ws = torch.empty(bl.workspace_size(bl.OP_FFN, m, hid, f), dtype=torch.uint8, device=dev)
+        for i in range(steps):
+            bl.ffn(x, g, u, d, workspace=ws)
     else:
         cfg = synth.WORKLOADS[4]
         m = cfg["m"]
@@ -370,7 +382,7 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--workload", choices=["default", "all"], default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "ffn1"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "ffn1", "ffn2048"], default=None,
                     help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 
