@@ -22,13 +22,13 @@ import os
 import torch
 
 __all__ = ["pack_weights", "quant_act", "forward", "ffn", "gemm_i32", "workspace_size",
-           "library_path", "load_library", "BitLinearError", "OP_PACK", "OP_FORWARD", "OP_FFN",
+           "library_path", "load_library", "BitLinearError", "OP_FORWARD", "OP_FFN", "OP_PACK",
            "OP_GEMM_I32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
-OP_PACK, OP_FORWARD, OP_FFN, OP_GEMM_I32 = 0, 1, 2, 3
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32 = 0, 1, 2, 3  # bl_op in include/bitlinear.h
 _F32, _BF16 = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -112,7 +112,25 @@ def _workspace(op: int, m: int, k: int, n: int, device) -> torch.Tensor | None:
 
 
 def _ws_args(ws):
-    return (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    return (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
+def _caller_workspace(ws: torch.Tensor, op: int, m: int, k: int, n: int) -> torch.Tensor | None:
+    """A caller-supplied workspace must be a contiguous device tensor of at least
+    workspace_size() bytes (the C ABI trusts the size it is given)."""
+    need = workspace_size(op, m, k, n)
+    if need == 0:
+        return None
+    _dev(ws, "workspace")
+    if ws.numel() * ws.element_size() < need:
+        raise BitLinearError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
+
+
+def _check_out(out: torch.Tensor, shape, dtype, name: str):
+    _dev(out, name, dtype)
+    if tuple(out.shape) != tuple(shape):
+        raise BitLinearError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
 
 
 def workspace_size(op: int, m: int, k: int, n: int) -> int:
@@ -152,9 +170,12 @@ def forward(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, *, retur
     n = packed.shape[0]
     if packed.shape[1] * 4 != k:
         raise BitLinearError("packed weights do not match the activation width")
+    if out is not None:
+        _check_out(out, (m, n), torch.float32, "out")
     y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if return_acc else None
-    ws = workspace if workspace is not None else _workspace(OP_FORWARD, m, k, n, x.device)
+    ws = (_caller_workspace(workspace, OP_FORWARD, m, k, n) if workspace is not None
+          else _workspace(OP_FORWARD, m, k, n, x.device))
     wp, wn = _ws_args(ws)
     _check(lib.bitlinear_forward(_dev(x, "x"), _act_dtype(x), m, k, _dev(packed, "packed", torch.uint8),
                                  _dev(gamma, "gamma", torch.float32), n, _dev(y, "y", torch.float32),
@@ -176,12 +197,15 @@ def ffn(x: torch.Tensor, gate, up, down, *, return_hq: bool = False,
     y = torch.empty((m, hidden), dtype=torch.float32, device=x.device)
     hq = torch.empty((m, ffn_dim), dtype=torch.int8, device=x.device) if return_hq else None
     hs = torch.empty(m, dtype=torch.float32, device=x.device) if return_hq else None
-    ws = workspace if workspace is not None else _workspace(OP_FFN, m, hidden, ffn_dim, x.device)
+    ws = (_caller_workspace(workspace, OP_FFN, m, hidden, ffn_dim) if workspace is not None
+          else _workspace(OP_FFN, m, hidden, ffn_dim, x.device))
     wp, wn = _ws_args(ws)
     _check(lib.bitlinear_ffn(_dev(x, "x"), _act_dtype(x), m, hidden, ffn_dim,
-                             _dev(gate[0], "gate_packed", torch.uint8), _dev(gate[1], "gate_gamma"),
-                             _dev(up[0], "up_packed", torch.uint8), _dev(up[1], "up_gamma"),
-                             _dev(down[0], "down_packed", torch.uint8), _dev(down[1], "down_gamma"),
+                             _dev(gate[0], "gate_packed", torch.uint8),
+                             _dev(gate[1], "gate_gamma", torch.float32),
+                             _dev(up[0], "up_packed", torch.uint8), _dev(up[1], "up_gamma", torch.float32),
+                             _dev(down[0], "down_packed", torch.uint8),
+                             _dev(down[1], "down_gamma", torch.float32),
                              y.data_ptr(), hq.data_ptr() if hq is not None else None,
                              hs.data_ptr() if hs is not None else None, wp, wn, _stream(x.device)),
            "bitlinear_ffn")

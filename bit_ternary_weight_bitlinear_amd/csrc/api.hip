@@ -138,7 +138,7 @@ size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n)
     }
 }
 
-const char *bitlinear_status_string(int status)
+const char *bitlinear_status_string(bl_status status)
 {
     switch (status) {
     case BL_OK: return "BL_OK";
@@ -164,7 +164,7 @@ bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k, uint8_t *
                                   static_cast<hipStream_t>(stream)));
 }
 
-bl_status bitlinear_quant_act(const void *x, int dtype, int64_t m, int64_t k, int8_t *q, float *scale,
+bl_status bitlinear_quant_act(const void *x, bl_dtype dtype, int64_t m, int64_t k, int8_t *q, float *scale,
                               void *stream)
 {
     if (!x || !q || !scale) return BL_ERR_NULL;
@@ -175,7 +175,7 @@ bl_status bitlinear_quant_act(const void *x, int dtype, int64_t m, int64_t k, in
                                        nullptr, static_cast<hipStream_t>(stream)));
 }
 
-bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k, const uint8_t *packed,
+bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k, const uint8_t *packed,
                             const float *gamma, int64_t n, float *y, int32_t *acc_out, void *workspace,
                             size_t workspace_bytes, void *stream)
 {
@@ -248,7 +248,7 @@ bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_
     return hip_status(launch_contraction(g, st));
 }
 
-bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int64_t ffn,
+bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden, int64_t ffn,
                         const uint8_t *gate_packed, const float *gate_gamma, const uint8_t *up_packed,
                         const float *up_gamma, const uint8_t *down_packed, const float *down_gamma,
                         float *y, int8_t *hq_out, float *hs_out, void *workspace, size_t workspace_bytes,

@@ -48,8 +48,10 @@ typedef enum {
 /* Element type of the activation input x. */
 typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 
-/* Operation selector for bitlinear_workspace_size(). */
-typedef enum { BL_OP_PACK = 0, BL_OP_FORWARD = 1, BL_OP_FFN = 2, BL_OP_GEMM_I32 = 3 } bl_op;
+/* Operation selector for bitlinear_workspace_size(): 0 = forward, 1 = FFN, as
+ * the two calls a layer makes per batch; the offline pack and the bare integer
+ * product follow. */
+typedef enum { BL_OP_FORWARD = 0, BL_OP_FFN = 1, BL_OP_PACK = 2, BL_OP_GEMM_I32 = 3 } bl_op;
 
 /* Largest supported dimension (k, n, hidden, ffn) and token count m. */
 #define BL_MAX_DIM ((int64_t)1 << 20)
@@ -57,12 +59,12 @@ typedef enum { BL_OP_PACK = 0, BL_OP_FORWARD = 1, BL_OP_FFN = 2, BL_OP_GEMM_I32 
 
 /*
  * Bytes of device workspace an operation needs (0 if none), for
- *   BL_OP_PACK:      (m ignored, k, n)
  *   BL_OP_FORWARD:   (m, k, n)
- *   BL_OP_GEMM_I32:  (m, k, n)
  *   BL_OP_FFN:       (m, hidden, ffn)   -- the last two arguments
- * Returns 0 for invalid shapes as well; the operation itself then reports the
- * shape error.
+ *   BL_OP_PACK:      (m ignored, k, n)
+ *   BL_OP_GEMM_I32:  (m, k, n)
+ * Returns 0 for invalid shapes and unknown ops as well; the operation itself
+ * then reports the shape error.
  */
 size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n);
 
@@ -96,7 +98,7 @@ bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
  *   scale    fp32 [m] (output): s = max(max_k |x|, 1e-5)
  * Requires k % 4 == 0.
  */
-bl_status bitlinear_quant_act(const void *x, int dtype, int64_t m, int64_t k,
+bl_status bitlinear_quant_act(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                               int8_t *q, float *scale, void *stream);
 
 /*
@@ -110,7 +112,7 @@ bl_status bitlinear_quant_act(const void *x, int dtype, int64_t m, int64_t k,
  *   workspace  >= bitlinear_workspace_size(BL_OP_FORWARD, m, k, n) bytes
  * Requires k % 4 == 0. No bias (the layer has none: section 架构创新).
  */
-bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k,
+bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                             const uint8_t *packed, const float *gamma, int64_t n,
                             float *y, int32_t *acc_out,
                             void *workspace, size_t workspace_bytes, void *stream);
@@ -133,7 +135,7 @@ bl_status bitlinear_forward(const void *x, int dtype, int64_t m, int64_t k,
  *   workspace    >= bitlinear_workspace_size(BL_OP_FFN, m, hidden, ffn) bytes
  * Requires hidden % 4 == 0 and ffn % 4 == 0.
  */
-bl_status bitlinear_ffn(const void *x, int dtype, int64_t m, int64_t hidden, int64_t ffn,
+bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden, int64_t ffn,
                         const uint8_t *gate_packed, const float *gate_gamma,
                         const uint8_t *up_packed, const float *up_gamma,
                         const uint8_t *down_packed, const float *down_gamma,
@@ -153,7 +155,7 @@ bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char *bitlinear_status_string(int status);
+const char *bitlinear_status_string(bl_status status);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP = range(7)
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32 = range(4)
 A = 0x10000          # aligned fake device address (never dereferenced)
 MIS = 0x10004        # 4-byte aligned only
 
@@ -51,13 +52,26 @@ def test_status_strings(lib):
 
 def test_workspace_size_rules(lib):
     ws = lib.bitlinear_workspace_size
-    assert ws(1, 1, 2560, 6912) == 0                       # decode path needs none
-    assert ws(1, 2048, 2560, 6912) >= 2048 * 2560            # qperm activations
-    assert ws(1, 1, 260, 7) >= 7 * 320 // 4                  # padded weight copy for ragged k
-    assert ws(0, 0, 4096, 14336) >= 14336 * 8                # per-row sums
-    assert ws(2, 1, 4096, 14336) >= 14336 * 4                # h buffer
-    assert ws(1, 0, 256, 256) == 0 and ws(1, 1, 6, 8) == 0   # invalid shapes
-    assert ws(9, 1, 256, 256) == 0
+    assert ws(OP_FORWARD, 1, 2560, 6912) == 0                     # decode path needs none
+    assert ws(OP_FORWARD, 2048, 2560, 6912) >= 2048 * 2560          # qperm activations
+    assert ws(OP_FORWARD, 1, 260, 7) >= 7 * 320 // 4                # padded weight copy for ragged k
+    assert ws(OP_PACK, 0, 4096, 14336) >= 14336 * 8                 # per-row sums
+    assert ws(OP_FFN, 1, 4096, 14336) >= 14336 * 4                  # h buffer
+    assert ws(OP_GEMM_I32, 1, 256, 8) >= 256 * 256                  # qperm copy of q
+    assert ws(OP_FORWARD, 0, 256, 256) == 0 and ws(OP_FORWARD, 1, 6, 8) == 0   # invalid shapes
+    assert ws(9, 1, 256, 256) == 0 and ws(-1, 1, 256, 256) == 0
+
+
+def test_op_numbering_matches_header():
+    """bl_op: 0 = forward and 1 = FFN (the two per-batch calls), then pack and
+    the bare integer product; the binding uses the same numbers."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum \{([^}]*)\} bl_op;", text).group(1)
+    vals = {k: int(v) for k, v in re.findall(r"(BL_OP_\w+)\s*=\s*(\d+)", body)}
+    assert vals == {"BL_OP_FORWARD": OP_FORWARD, "BL_OP_FFN": OP_FFN, "BL_OP_PACK": OP_PACK,
+                    "BL_OP_GEMM_I32": OP_GEMM_I32}
+    import bit_ternary_weight_bitlinear_amd as bl
+    assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32) == (0, 1, 2, 3)
 
 
 def test_forward_argument_errors(lib):
@@ -73,12 +87,12 @@ def test_forward_argument_errors(lib):
     assert f(A, 0, 1, (1 << 20) + 4, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
     assert f(A, 0, 1, 256, A, A, (1 << 20) + 1, A, None, None, 0, None) == BL_ERR_SHAPE
     assert f(A, 0, (1 << 22) + 1, 256, A, A, 8, A, None, None, 0, None) == BL_ERR_SHAPE
-    assert lib.bitlinear_workspace_size(1, 1 << 22, 4, 3) > 0
-    assert lib.bitlinear_workspace_size(1, (1 << 22) + 1, 4, 3) == 0
+    assert lib.bitlinear_workspace_size(OP_FORWARD, 1 << 22, 4, 3) > 0
+    assert lib.bitlinear_workspace_size(OP_FORWARD, (1 << 22) + 1, 4, 3) == 0
     assert f(MIS, 0, 1, 256, A, A, 8, A, None, None, 0, None) == BL_ERR_ALIGN
     assert f(A, 0, 1, 256, MIS, A, 8, A, None, None, 0, None) == BL_ERR_ALIGN
     assert f(A, 0, 1, 256, A, A, 8, A, MIS, None, 0, None) == BL_ERR_ALIGN
-    need = lib.bitlinear_workspace_size(1, 64, 256, 8)
+    need = lib.bitlinear_workspace_size(OP_FORWARD, 64, 256, 8)
     assert f(A, 1, 64, 256, A, A, 8, A, None, None, 0, None) == BL_ERR_NULL
     assert f(A, 1, 64, 256, A, A, 8, A, None, A, need - 1, None) == BL_ERR_WORKSPACE
     assert f(A, 1, 64, 256, A, A, 8, A, None, A + 16, need, None) == BL_ERR_ALIGN
