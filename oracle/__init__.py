@@ -14,10 +14,15 @@ the order the pages give:
   ffn:      one quantization of x shared by gate and up  ->  h = relu(g)^2 * u
             ->  per-token requantization of h  ->  down projection
 
+  threshold pack (a second weight quantizer): delta = factor * mean|W|
+            ->  W~ = sign(W) where |W| > delta, else 0  ->  alpha = mean(|W| * mask)
+            ->  the same 2-bit codes; alpha takes gamma's place in forward/ffn
+
 Sources: "BitNet 1-bit LLM 的混合精度微调技术：渐进量化策略" (BitLinear paragraph,
 operational-parameter paragraph); "BitNet 中使用直通估计器工程化三元权重训练"
 (section 工程化训练流程与参数配置, activation item); "穿越1比特的奇幻旅程" summary of
-the BitNet b1.58 2B4T report (sections 架构创新 and 推理实现 / GPU端).
+the BitNet b1.58 2B4T report (sections 架构创新 and 推理实现 / GPU端); "BitNet
+三元权重阈值优化工程实践" (section on the core principle of threshold optimization).
 
 Parity pins for every function live in tests/test_oracle_pins.py; none of them
 is "parity unpinned".
@@ -48,6 +53,8 @@ def _load():
     lib.oracle_absmean.restype = ctypes.c_float
     lib.oracle_absmean.argtypes = [_p, _i64, _i64]
     lib.oracle_ternarize.argtypes = [_p, _i64, _i64, ctypes.c_float, _p]
+    lib.oracle_threshold_ternarize.restype = ctypes.c_float
+    lib.oracle_threshold_ternarize.argtypes = [_p, _i64, _i64, ctypes.c_float, _p, _p]
     lib.oracle_pack.argtypes = [_p, _i64, _i64, _p]
     lib.oracle_unpack.restype = _i64
     lib.oracle_unpack.argtypes = [_p, _i64, _i64, _p]
@@ -129,6 +136,22 @@ def pack_weights(w: np.ndarray):
     g = absmean(w)
     wt = ternarize(w, g)
     return pack(wt), g, wt
+
+
+def threshold_ternarize(w: np.ndarray, factor: float = 0.7):
+    """(ternary int8 [n][k], alpha fp32, delta fp32) of the threshold quantizer."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    wt = np.empty((n, k), dtype=np.int8)
+    delta = np.zeros(1, dtype=np.float32)
+    alpha = _load().oracle_threshold_ternarize(_ptr(w), n, k, float(np.float32(factor)), _ptr(wt), _ptr(delta))
+    return wt, np.float32(alpha), delta[0]
+
+
+def pack_weights_threshold(w: np.ndarray, factor: float = 0.7):
+    """Threshold weight step: (packed uint8 [n][k/4], alpha fp32, ternary int8, delta fp32)."""
+    wt, alpha, delta = threshold_ternarize(w, factor)
+    return pack(wt), alpha, wt, delta
 
 
 def _as_f32_acts(x, dtype: str):

@@ -13,6 +13,9 @@
  *  [P3] "穿越1比特的奇幻旅程：高效语言模型的未来之谜" (beiduofen.top; summary of
  *       the BitNet b1.58 2B4T Technical Report), sections "架构创新" and
  *       "推理实现 / GPU端".
+ *  [P4] "BitNet 三元权重阈值优化工程实践" (blog.hotdry.top, 2025-09-08), section
+ *       on the core principle of ternary threshold optimization (the threshold
+ *       quantizer and its code).
  *
  * Every function is a direct loop over the definition. Floating point follows
  * the precision the kernels decide integers in (fp32), with the operation order
@@ -93,6 +96,40 @@ void oracle_ternarize(const float *w, int64_t n, int64_t k, float gamma, int8_t 
         if (r < -1.0f) r = -1.0f;
         wt[i] = (int8_t)r;
     }
+}
+
+/* Threshold ternarization [P4, section on the core principle]: a weight is kept
+ * (as its sign) when its magnitude exceeds delta = factor * mean|W|, and the
+ * layer's scale is the mean over all n*k weights of |w| times that mask.
+ * Readings: mean|W| is the absmean above (same fixed fp64 order, one fp32
+ * rounding); delta is the fp32 product factor * mean; the mask is a strict
+ * |w| > delta in fp32; the masked magnitudes are summed in fp64 in the same
+ * fixed order as the absmean and divided by n*k (not by the number kept),
+ * then rounded once to fp32. Writes the ternary weights and delta; returns
+ * the scale alpha. */
+float oracle_threshold_ternarize(const float *w, int64_t n, int64_t k, float factor, int8_t *wt,
+                                 float *delta_out)
+{
+    const float mean = oracle_absmean(w, n, k);
+    const float delta = factor * mean;
+    double total = 0.0;
+    for (int64_t r = 0; r < n; ++r) {
+        double row = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            const float v = w[r * k + c];
+            const float a = fabsf(v);
+            if (a > delta) {
+                row += (double)a;
+                wt[r * k + c] = (int8_t)((v > 0.0f) - (v < 0.0f));
+            } else {
+                wt[r * k + c] = 0;
+            }
+        }
+        total += row;
+    }
+    *delta_out = delta;
+    const double kept_mean = total / ((double)n * (double)k);
+    return (float)kept_mean;
 }
 
 /* Four ternary weights per byte [P3 推理实现 / GPU端]; code = w + 1 in {0,1,2};

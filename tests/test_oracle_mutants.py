@@ -2,8 +2,10 @@
 
 Each case copies the oracle into a temporary tree, plants one mistake in the C
 source (a wrong tie rule, bit order, scale, dropped term, transposed operand,
-missing clip, signed absmax), rebuilds it with gcc and runs the pin tests
-against that copy in a subprocess; at least one pin must fail.
+missing clip, signed absmax; for the threshold quantizer a non-strict
+comparison, a dropped factor or sign, the mean over the kept weights only),
+rebuilds it with gcc and runs every oracle pin file against that copy in a
+subprocess; at least one pin must fail.
 """
 import os
 import shutil
@@ -24,7 +26,19 @@ MUTANTS = [
     ("if (r < -1.0f) r = -1.0f;", ""),                                     # one-sided clip
     ("(int32_t)wt[r * k + c]", "(int32_t)wt[c * n + r]"),                  # transposed weights
     ("if (a > amax) amax = a;", "if (row[c] > amax) amax = row[c];"),      # max x, not max|x|
+    # threshold quantizer
+    ("if (a > delta) {", "if (a >= delta) {"),                              # >= instead of strict >
+    ("const float delta = factor * mean;", "const float delta = mean;"),    # factor dropped
+    ("(int8_t)((v > 0.0f) - (v < 0.0f))", "(int8_t)1"),                    # sign dropped
+    ("row += (double)a;", "row += (double)a; kept += 1.0;"),                # alpha over the kept count
 ]
+# the kept-count mutant also needs its counter declared and used
+EXTRA = {
+    "row += (double)a; kept += 1.0;": [("double total = 0.0;\n    for (int64_t r = 0; r < n; ++r) {\n        double row = 0.0;\n        for (int64_t c = 0; c < k; ++c) {\n            const float v",
+                                        "double total = 0.0, kept = 0.0;\n    for (int64_t r = 0; r < n; ++r) {\n        double row = 0.0;\n        for (int64_t c = 0; c < k; ++c) {\n            const float v"),
+                                       ("const double kept_mean = total / ((double)n * (double)k);",
+                                        "const double kept_mean = kept > 0.0 ? total / kept : 0.0;")],
+}
 
 
 @pytest.mark.parametrize("old,new", MUTANTS)
@@ -34,11 +48,16 @@ def test_pins_catch_planted_mistake(tmp_path, old, new):
                         ignore=shutil.ignore_patterns("*.so", "__pycache__", "test_oracle_mutants.py"))
     src = tmp_path / "oracle" / "bitlinear_oracle.c"
     text = src.read_text()
-    assert old in text
-    src.write_text(text.replace(old, new))
+    assert text.count(old) == 1, old
+    text = text.replace(old, new)
+    for a, b in EXTRA.get(new, []):
+        assert text.count(a) == 1, a
+        text = text.replace(a, b)
+    src.write_text(text)
     subprocess.run([sys.executable, str(tmp_path / "oracle" / "build.py")], check=True,
                    stdout=subprocess.DEVNULL)
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
-                       text=True, timeout=600)
+    pins = sorted(f"tests/{f}" for f in os.listdir(tmp_path / "tests")
+                  if f.startswith("test_oracle_pins") and f.endswith(".py"))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *pins],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "planted mistake went unnoticed:\n" + r.stdout[-2000:]
