@@ -14,6 +14,9 @@ the order the pages give:
   ffn:      one quantization of x shared by gate and up  ->  h = relu(g)^2 * u
             ->  per-token requantization of h  ->  down projection
 
+  rms norm (subln) before the activation quantization, per token:
+            S = sum_k x^2 (correctly rounded fp64)  ->  ms = fp32(S / k)
+            ->  r = 1 / sqrt(ms + 1e-5) (fp32)  ->  x^ = (x * r) * g  ->  absmax int8 of x^
   threshold pack (a second weight quantizer): delta = factor * mean|W|
             ->  W~ = sign(W) where |W| > delta, else 0  ->  alpha = mean(|W| * mask)
             ->  the same 2-bit codes; alpha takes gamma's place in forward/ffn
@@ -30,6 +33,7 @@ is "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -172,6 +176,43 @@ def quant_act(x: np.ndarray, dtype: str = "f32"):
     return q, s
 
 
+NORM_EPS = np.float32(1e-5)
+
+
+def rms_norm(x: np.ndarray, dtype: str = "f32", gain: np.ndarray | None = None) -> np.ndarray:
+    """Per-token RMS normalization ("subln" of "穿越1比特的奇幻旅程", section 架构创新:
+    a normalization added for the stability of 1-bit training; "BitNet 中使用直通估计器
+    工程化三元权重训练", section 工程化训练流程与参数配置: layer normalization keeps the
+    variance, epsilon 1e-5). Reading: RMSNorm without mean subtraction or bias,
+    an optional per-channel gain g, epsilon 1e-5 inside the square root:
+      S  = sum_k x_k^2      every square exact in fp64, the sum correctly rounded
+                            to fp64 (math.fsum)
+      ms = fp32(S / k)      one fp64 division, one rounding to fp32
+      r  = 1 / sqrt(ms + 1e-5)          each fp32 operation correctly rounded
+      x^ = (x * r) * g      fp32, in that order (x * r without a gain)
+    Returns x^ as fp32 [m][k]."""
+    xf = _as_f32_acts(x, dtype)
+    m, k = xf.shape
+    g = None if gain is None else _c(gain, np.float32).reshape(k)
+    out = np.empty((m, k), dtype=np.float32)
+    for t in range(m):
+        sq = xf[t].astype(np.float64) ** 2
+        s_sum = math.fsum(sq.tolist())
+        ms = np.float32(s_sum / k)
+        d = np.float32(ms + NORM_EPS)
+        r = np.float32(np.float32(1.0) / np.sqrt(d))
+        row = xf[t] * r
+        if g is not None:
+            row = row * g
+        out[t] = row
+    return out
+
+
+def quant_act_norm(x: np.ndarray, dtype: str = "f32", gain: np.ndarray | None = None):
+    """(q int8 [m][k], s fp32 [m]) of the absmax quantization of rms_norm(x)."""
+    return quant_act(rms_norm(x, dtype, gain), "f32")
+
+
 def matmul_i32(q: np.ndarray, wt: np.ndarray) -> np.ndarray:
     q = _c(q, np.int8)
     wt = _c(wt, np.int8)
@@ -210,6 +251,15 @@ def forward(x: np.ndarray, packed: np.ndarray, gamma, k: int, dtype: str = "f32"
     acc = matmul_i32(q, wt)
     y = rescale(acc, s, gamma)
     return dict(q=q, s=s, acc=acc, y=y)
+
+
+def forward_norm(x: np.ndarray, packed: np.ndarray, gamma, k: int, dtype: str = "f32",
+                 gain: np.ndarray | None = None):
+    """BitLinear forward with the RMS norm before the quantization. dict(xn, q, s, acc, y)."""
+    xn = rms_norm(x, dtype, gain)
+    r = forward(xn, packed, gamma, k, "f32")
+    r["xn"] = xn
+    return r
 
 
 def ffn(x: np.ndarray, gate, up, down, hidden: int, ffn_dim: int, dtype: str = "bf16"):

@@ -41,12 +41,21 @@ EXTRA = {
 }
 
 
-@pytest.mark.parametrize("old,new", MUTANTS)
-def test_pins_catch_planted_mistake(tmp_path, old, new):
+# mistakes planted in the Python part of the oracle (the RMS norm)
+PY_MUTANTS = [
+    ("ms = np.float32(s_sum / k)", "ms = np.float32(s_sum / (k - 1))"),              # biased mean
+    ("d = np.float32(ms + NORM_EPS)", "d = np.float32(ms)"),                           # epsilon dropped
+    ("r = np.float32(np.float32(1.0) / np.sqrt(d))", "r = np.float32(np.float32(1.0) / d)"),  # no square root
+    ("            row = row * g", "            row = row"),                           # gain dropped
+]
+
+
+@pytest.mark.parametrize("old,new,lang", [(o, n, "c") for o, n in MUTANTS] + [(o, n, "py") for o, n in PY_MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, old, new, lang):
     for d in ("oracle", "synth", "tests"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__", "test_oracle_mutants.py"))
-    src = tmp_path / "oracle" / "bitlinear_oracle.c"
+    src = tmp_path / "oracle" / ("bitlinear_oracle.c" if lang == "c" else "__init__.py")
     text = src.read_text()
     assert text.count(old) == 1, old
     text = text.replace(old, new)
