@@ -7,6 +7,7 @@ call raises -- there is no fallback.
 
 Functions mirror the C entry points:
   pack_weights(w)                      -> (packed uint8 [n][k/4], gamma fp32 [1])
+  pack_weights_threshold(w, factor)    -> (packed uint8 [n][k/4], alpha fp32 [1], delta fp32 [1])
   quant_act(x)                         -> (q int8 [m][k], scale fp32 [m])
   forward(x, packed, gamma)            -> y fp32 [m][n]        (return_acc=True adds acc)
   ffn(x, gate, up, down)               -> y fp32 [m][hidden]   (return_hq=True adds qh, sh)
@@ -21,14 +22,14 @@ import os
 
 import torch
 
-__all__ = ["pack_weights", "quant_act", "forward", "ffn", "gemm_i32", "workspace_size",
+__all__ = ["pack_weights", "pack_weights_threshold", "quant_act", "forward", "ffn", "gemm_i32", "workspace_size",
            "library_path", "load_library", "BitLinearError", "OP_FORWARD", "OP_FFN", "OP_PACK",
-           "OP_GEMM_I32"]
+           "OP_GEMM_I32", "OP_PACK_THRESHOLD"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32 = 0, 1, 2, 3  # bl_op in include/bitlinear.h
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD = 0, 1, 2, 3, 4  # bl_op in include/bitlinear.h
 _F32, _BF16 = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -40,6 +41,8 @@ _SIGNATURES = {
     "bitlinear_workspace_size": (_c_size, [_c_int, _c_i64, _c_i64, _c_i64]),
     "bitlinear_status_string": (ctypes.c_char_p, [_c_int]),
     "bitlinear_pack_weights": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_size, _c_p]),
+    "bitlinear_pack_weights_threshold": (_c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p,
+                                                  _c_p, _c_size, _c_p]),
     "bitlinear_quant_act": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "bitlinear_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p,
                                    _c_p, _c_size, _c_p]),
@@ -149,6 +152,22 @@ def pack_weights(w: torch.Tensor):
                                       gamma.data_ptr(), wp, wn, _stream(w.device)),
            "bitlinear_pack_weights")
     return packed, gamma
+
+
+def pack_weights_threshold(w: torch.Tensor, factor: float = 0.7):
+    """fp32 weights [n][k] -> (packed uint8 [n][k/4], alpha fp32 [1], delta fp32 [1]) of the
+    threshold quantizer; (packed, alpha) is used like (packed, gamma)."""
+    lib = load_library()
+    n, k = w.shape
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    alpha = torch.empty(1, dtype=torch.float32, device=w.device)
+    delta = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = _workspace(OP_PACK_THRESHOLD, 0, k, n, w.device)
+    wp, wn = _ws_args(ws)
+    _check(lib.bitlinear_pack_weights_threshold(_dev(w, "w", torch.float32), n, k, float(factor),
+                                                packed.data_ptr(), alpha.data_ptr(), delta.data_ptr(), wp, wn,
+                                                _stream(w.device)), "bitlinear_pack_weights_threshold")
+    return packed, alpha, delta
 
 
 def quant_act(x: torch.Tensor):

@@ -105,6 +105,20 @@ FfnLayout ffn_layout(void *ws, int64_t m, int64_t hidden, int64_t ffn)
 
 bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
+// argument checks of the forward (shared by bitlinear_forward and its variant
+// without a workspace argument)
+bl_status forward_args(const void *x, bl_dtype dtype, int64_t m, int64_t k, const uint8_t *packed,
+                       const float *gamma, int64_t n, const float *y, const int32_t *acc_out)
+{
+    if (!x || !packed || !gamma || !y) return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return BL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned(gamma, 4) ||
+        (acc_out && !aligned16(acc_out)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
 bl_status check_ws(void *ws, size_t ws_bytes, int64_t need)
 {
     if (need == 0) return BL_OK;
@@ -133,6 +147,9 @@ size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n)
     case BL_OP_FFN:
         if (!tokens_ok(m) || !kdim_ok(k) || !kdim_ok(n)) return 0;
         return (size_t)ffn_layout(nullptr, m, k, n).bytes;
+    case BL_OP_PACK_THRESHOLD:
+        if (!dim_ok(n) || !kdim_ok(k)) return 0;
+        return (size_t)(round_up(n * 8, kAlign) + kAlign);
     default:
         return 0;
     }
@@ -148,6 +165,7 @@ const char *bitlinear_status_string(bl_status status)
     case BL_ERR_DTYPE: return "BL_ERR_DTYPE: unknown activation dtype";
     case BL_ERR_WORKSPACE: return "BL_ERR_WORKSPACE: workspace smaller than bitlinear_workspace_size()";
     case BL_ERR_HIP: return "BL_ERR_HIP: a kernel launch failed";
+    case BL_ERR_VALUE: return "BL_ERR_VALUE: a scalar argument is out of range";
     default: return "unknown bitlinear status";
     }
 }
@@ -162,6 +180,23 @@ bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k, uint8_t *
     if (ws != BL_OK) return ws;
     return hip_status(launch_pack(w, n, k, packed, gamma, static_cast<double *>(workspace),
                                   static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_pack_weights_threshold(const float *w, int64_t n, int64_t k, float delta_factor,
+                                           uint8_t *packed, float *alpha, float *delta_out, void *workspace,
+                                           size_t workspace_bytes, void *stream)
+{
+    if (!w || !packed || !alpha) return BL_ERR_NULL;
+    if (!dim_ok(n) || !kdim_ok(k)) return BL_ERR_SHAPE;
+    if (!(delta_factor >= 0.0f) || !(delta_factor <= 3.402823466e38f)) return BL_ERR_VALUE;  // NaN fails both
+    if (!aligned16(w) || !aligned16(packed) || !aligned(alpha, 4) || (delta_out && !aligned(delta_out, 4)))
+        return BL_ERR_ALIGN;
+    const int64_t sums = round_up(n * 8, kAlign);
+    const bl_status ws = check_ws(workspace, workspace_bytes, sums + kAlign);
+    if (ws != BL_OK) return ws;
+    float *delta = delta_out ? delta_out : reinterpret_cast<float *>(static_cast<char *>(workspace) + sums);
+    return hip_status(launch_pack_threshold(w, n, k, delta_factor, packed, alpha, delta,
+                                            static_cast<double *>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 bl_status bitlinear_quant_act(const void *x, bl_dtype dtype, int64_t m, int64_t k, int8_t *q, float *scale,
@@ -179,12 +214,7 @@ bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                             const float *gamma, int64_t n, float *y, int32_t *acc_out, void *workspace,
                             size_t workspace_bytes, void *stream)
 {
-    if (!x || !packed || !gamma || !y) return BL_ERR_NULL;
-    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
-    if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return BL_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned(gamma, 4) ||
-        (acc_out && !aligned16(acc_out)))
-        return BL_ERR_ALIGN;
+    if (const bl_status a = forward_args(x, dtype, m, k, packed, gamma, n, y, acc_out)) return a;
     const FwdLayout need = forward_layout(nullptr, m, k, n, false);
     const bl_status wss = check_ws(workspace, workspace_bytes, need.bytes);
     if (wss != BL_OK) return wss;

@@ -11,6 +11,11 @@ namespace bl {
 hipError_t launch_pack(const float *w, int64_t n, int64_t k, uint8_t *packed, float *gamma,
                        double *rowsum, hipStream_t st);
 
+// threshold quantizer: delta = factor * mean|W| (into delta[0]), codes sign(w) where
+// |w| > delta, alpha = mean(|W| * mask); workspace: n doubles
+hipError_t launch_pack_threshold(const float *w, int64_t n, int64_t k, float factor, uint8_t *packed,
+                                 float *alpha, float *delta, double *rowsum, hipStream_t st);
+
 // copies packed rows [n][k/4] into a zero-weight padded layout [n][kp/4] (code 1 in the tail)
 hipError_t launch_pad_weights(const uint8_t *src, int64_t n, int64_t k, int64_t kp, uint8_t *dst,
                               hipStream_t st);

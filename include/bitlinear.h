@@ -42,7 +42,8 @@ typedef enum {
     BL_ERR_ALIGN = 3,      /* a device pointer is not 16-byte aligned           */
     BL_ERR_DTYPE = 4,      /* unknown activation dtype                          */
     BL_ERR_WORKSPACE = 5,  /* workspace smaller than bitlinear_workspace_size() */
-    BL_ERR_HIP = 6         /* a kernel launch failed                            */
+    BL_ERR_HIP = 6,        /* a kernel launch failed                            */
+    BL_ERR_VALUE = 7       /* a scalar argument is out of range                 */
 } bl_status;
 
 /* Element type of the activation input x. */
@@ -51,7 +52,13 @@ typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 /* Operation selector for bitlinear_workspace_size(): 0 = forward, 1 = FFN, as
  * the two calls a layer makes per batch; the offline pack and the bare integer
  * product follow. */
-typedef enum { BL_OP_FORWARD = 0, BL_OP_FFN = 1, BL_OP_PACK = 2, BL_OP_GEMM_I32 = 3 } bl_op;
+typedef enum {
+    BL_OP_FORWARD = 0,
+    BL_OP_FFN = 1,
+    BL_OP_PACK = 2,
+    BL_OP_GEMM_I32 = 3,
+    BL_OP_PACK_THRESHOLD = 4
+} bl_op;
 
 /* Largest supported dimension (k, n, hidden, ffn) and token count m. */
 #define BL_MAX_DIM ((int64_t)1 << 20)
@@ -63,6 +70,7 @@ typedef enum { BL_OP_FORWARD = 0, BL_OP_FFN = 1, BL_OP_PACK = 2, BL_OP_GEMM_I32 
  *   BL_OP_FFN:       (m, hidden, ffn)   -- the last two arguments
  *   BL_OP_PACK:      (m ignored, k, n)
  *   BL_OP_GEMM_I32:  (m, k, n)
+ *   BL_OP_PACK_THRESHOLD: (m ignored, k, n)
  * Returns 0 for invalid shapes and unknown ops as well; the operation itself
  * then reports the shape error.
  */
@@ -80,13 +88,39 @@ size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n);
  *            divided by n*k and rounded once to fp32. Weights quantize to
  *            clip(rint(w / gamma), -1, 1) with a correctly rounded fp32
  *            division and ties to even; gamma = 0 quantizes every weight to 0.
- *   workspace  >= bitlinear_workspace_size(BL_OP_PACK, 0, k, n) bytes.
+ *   workspace  >= bitlinear_workspace_size(BL_OP_PACK, 0, k, n) bytes: the
+ *            fp64 row sums of the fixed summation order (one per row), which
+ *            the library may not allocate itself.
  * Requires k % 4 == 0.
  */
 bl_status bitlinear_pack_weights(const float *w, int64_t n, int64_t k,
                                  uint8_t *packed, float *gamma,
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/*
+ * Offline weight quantization with a magnitude threshold ("BitNet 三元权重阈值
+ * 优化工程实践", section on the core principle of ternary threshold optimization:
+ * the threshold is a factor -- 0.7 by default, 0.6-0.75 per layer kind -- times
+ * mean|W|; weights above it keep their sign, the rest become 0; the scale is
+ * the mean of the kept magnitudes over the whole tensor).
+ *   w             fp32 [n][k] weights (input)
+ *   delta_factor  finite, >= 0 (else BL_ERR_VALUE)
+ *   packed        uint8 [n][k/4] (output): the same 2-bit layout as
+ *                 bitlinear_pack_weights, code = w~ + 1 with
+ *                 w~ = sign(w) if |w| > delta (strict), else 0
+ *   alpha         fp32 [1] (output): sum of |w| over the kept weights divided by
+ *                 n*k (all weights), accumulated in fp64 in the fixed order of
+ *                 bitlinear_pack_weights, rounded once to fp32. alpha takes
+ *                 gamma's place in bitlinear_forward and bitlinear_ffn.
+ *   delta_out     optional fp32 [1] (output): delta = delta_factor * mean|W| as
+ *                 one fp32 product, mean|W| exactly as gamma above; NULL skips it
+ *   workspace     >= bitlinear_workspace_size(BL_OP_PACK_THRESHOLD, 0, k, n) bytes
+ * Requires k % 4 == 0.
+ */
+bl_status bitlinear_pack_weights_threshold(const float *w, int64_t n, int64_t k, float delta_factor,
+                                           uint8_t *packed, float *alpha, float *delta_out,
+                                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Per-token absmax activation quantization to int8 ("BitNet 1-bit LLM 的混合精度
@@ -148,7 +182,8 @@ bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden
  *   q        int8 [m][k] (input, natural layout)
  *   packed   uint8 [n][k/4]
  *   acc      int32 [m][n] (output): sum_k q[m][k] * w~[n][k], exact
- *   workspace  >= bitlinear_workspace_size(BL_OP_GEMM_I32, m, k, n) bytes
+ *   workspace  >= bitlinear_workspace_size(BL_OP_GEMM_I32, m, k, n) bytes: the
+ *            kernels read q in an internal permuted layout, copied there first
  */
 bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k,
                              const uint8_t *packed, int64_t n, int32_t *acc,

@@ -11,8 +11,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
-BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP = range(7)
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32 = range(4)
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, BL_ERR_VALUE = range(8)
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD = range(5)
 A = 0x10000          # aligned fake device address (never dereferenced)
 MIS = 0x10004        # 4-byte aligned only
 
@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward", "bitlinear_ffn",
-              "bitlinear_gemm_i32", "bitlinear_workspace_size", "bitlinear_status_string"):
+              "bitlinear_gemm_i32", "bitlinear_workspace_size", "bitlinear_status_string",
+              "bitlinear_pack_weights_threshold"):
         assert n in names
 
 
@@ -45,8 +46,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.bitlinear_status_string(s)
+        assert not lib.bitlinear_status_string(s).startswith(b"unknown")
     assert b"unknown" in lib.bitlinear_status_string(99)
 
 
@@ -69,9 +71,9 @@ def test_op_numbering_matches_header():
     body = re.search(r"typedef enum \{([^}]*)\} bl_op;", text).group(1)
     vals = {k: int(v) for k, v in re.findall(r"(BL_OP_\w+)\s*=\s*(\d+)", body)}
     assert vals == {"BL_OP_FORWARD": OP_FORWARD, "BL_OP_FFN": OP_FFN, "BL_OP_PACK": OP_PACK,
-                    "BL_OP_GEMM_I32": OP_GEMM_I32}
+                    "BL_OP_GEMM_I32": OP_GEMM_I32, "BL_OP_PACK_THRESHOLD": OP_PACK_THRESHOLD}
     import bit_ternary_weight_bitlinear_amd as bl
-    assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32) == (0, 1, 2, 3)
+    assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32, bl.OP_PACK_THRESHOLD) == (0, 1, 2, 3, 4)
 
 
 def test_forward_argument_errors(lib):
@@ -107,6 +109,19 @@ def test_other_entry_points_argument_errors(lib):
     assert lib.bitlinear_quant_act(A, 1, 1, 256, MIS, A, None) == BL_ERR_ALIGN
     assert lib.bitlinear_gemm_i32(A, 4, 256, A, 8, None, A, 1 << 20, None) == BL_ERR_NULL
     assert lib.bitlinear_gemm_i32(A, 4, 256, A, 8, A, A, 0, None) == BL_ERR_WORKSPACE
+    t = lib.bitlinear_pack_weights_threshold
+    t.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    need = lib.bitlinear_workspace_size(OP_PACK_THRESHOLD, 0, 256, 8)
+    assert need >= 8 * 8
+    assert t(None, 8, 256, 0.7, A, A, None, A, need, None) == BL_ERR_NULL
+    assert t(A, 8, 256, 0.7, A, None, None, A, need, None) == BL_ERR_NULL
+    assert t(A, 8, 250, 0.7, A, A, None, A, need, None) == BL_ERR_SHAPE
+    for bad in (-0.1, float("nan"), float("inf")):
+        assert t(A, 8, 256, bad, A, A, None, A, need, None) == BL_ERR_VALUE
+    assert t(A, 8, 256, 0.7, A, A, MIS + 1, A, need, None) == BL_ERR_ALIGN
+    assert t(A, 8, 256, 0.7, A, A, None, A, need - 1, None) == BL_ERR_WORKSPACE
+    assert t(A, 8, 256, 0.7, A, A, None, None, need, None) == BL_ERR_NULL
     ffn = lib.bitlinear_ffn
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, None, A, A, None, None, A, 1 << 20, None) == BL_ERR_NULL
     assert ffn(A, 1, 1, 256, 510, A, A, A, A, A, A, A, None, None, A, 1 << 20, None) == BL_ERR_SHAPE

@@ -303,3 +303,40 @@ def test_graph_replay_matches_eager(bl, m, k, n):
         # unrelated eager work on the same buffers between replays
         bl.forward(x * 2, packed, gamma, out=y, workspace=ws if ws_bytes else None)
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ threshold quantizer
+
+@pytest.mark.parametrize("n,k,factor", [(1, 4, 0.7), (7, 260, 0.7), (256, 256, 0.6), (300, 2560, 0.75),
+                                        (6912, 2560, 0.7), (14336, 4096, 0.7), (5, 64, 0.0)])
+def test_pack_threshold_bit_exact(bl, n, k, factor):
+    w = synth.weights(98, 1, n, k)
+    p_ref, a_ref, _, d_ref = oracle.pack_weights_threshold(w, factor)
+    packed, alpha, delta = bl.pack_weights_threshold(to_dev(w), factor)
+    assert host(delta)[0].view(np.uint32) == np.float32(d_ref).view(np.uint32)
+    assert host(alpha)[0].view(np.uint32) == np.float32(a_ref).view(np.uint32)
+    np.testing.assert_array_equal(host(packed), p_ref)
+
+
+def test_pack_threshold_hand_worked(bl, golden):
+    for c in golden["threshold_cases"]:
+        packed, alpha, delta = bl.pack_weights_threshold(to_dev(np.array(c["w"], np.float32)), c["factor"])
+        assert host(delta)[0] == np.float32(c["delta"]) and host(alpha)[0] == np.float32(c["alpha"])
+        np.testing.assert_array_equal(host(packed), np.array(c["packed"], np.uint8))
+        if "x_f32" in c:
+            y, acc = bl.forward(to_dev(np.array(c["x_f32"], np.float32)), packed, alpha, return_acc=True)
+            np.testing.assert_array_equal(host(acc), c["acc"])
+            np.testing.assert_array_equal(host(y), np.array(c["y"], np.float32))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (8, 2560, 700), (300, 6912, 256)])
+def test_forward_threshold_weights(bl, m, k, n):
+    """The threshold quantizer's codes and alpha go through the same forward."""
+    w = synth.weights(99, 1, n, k)
+    x = synth.activations(99, m, k, dtype="bf16")
+    p_ref, a_ref, _, _ = oracle.pack_weights_threshold(w, 0.7)
+    packed, alpha, _ = bl.pack_weights_threshold(to_dev(w), 0.7)
+    y, acc = bl.forward(to_dev(x, "bf16"), packed, alpha, return_acc=True)
+    r = oracle.forward(x, p_ref, a_ref, k, "bf16")
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
