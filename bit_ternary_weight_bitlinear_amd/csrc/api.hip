@@ -5,6 +5,7 @@
 // caller's stream. Nothing here allocates, synchronises or keeps state.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/bitlinear.h"
@@ -116,6 +117,36 @@ bl_status forward_args(const void *x, bl_dtype dtype, int64_t m, int64_t k, cons
     if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned(gamma, 4) ||
         (acc_out && !aligned16(acc_out)))
         return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+// ---- the library-owned scratch of bitlinear_forward_noalloc
+// One array per device, in the code object's zero-initialised data (no file
+// space), held by every device the library runs on until the process ends.
+// Its device address is looked up once per device and cached; host code never
+// passes the symbol itself to a kernel (on the host it is only a stand-in).
+static __device__ __align__(256) uint8_t scratch[BL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+bl_status scratch_address(hipStream_t st, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BL_ERR_HIP;
+    if (st) {
+        int sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) != hipSuccess) return BL_ERR_HIP;
+        if (sdev != dev) return BL_ERR_VALUE;  // the stream must belong to the current device
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BL_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return BL_OK;
 }
 
@@ -251,6 +282,20 @@ bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
     g.out = y; g.acc_out = acc_out; g.epi = EPI_Y;
     return hip_status(launch_contraction(g, st));
+}
+
+bl_status bitlinear_forward_noalloc(const void *x, bl_dtype dtype, int64_t m, int64_t k, const uint8_t *packed,
+                                    const float *gamma, int64_t n, float *y, int32_t *acc_out, void *stream)
+{
+    if (const bl_status a = forward_args(x, dtype, m, k, packed, gamma, n, y, acc_out)) return a;
+    const int64_t need = forward_layout(nullptr, m, k, n, false).bytes;
+    if (need > BL_NOALLOC_SCRATCH_BYTES) return BL_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        if (const bl_status e = scratch_address(static_cast<hipStream_t>(stream), &ws)) return e;
+    }
+    return bitlinear_forward(x, dtype, m, k, packed, gamma, n, y, acc_out, ws,
+                             need > 0 ? (size_t)BL_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_t *packed, int64_t n,

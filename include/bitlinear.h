@@ -16,6 +16,8 @@
  *    enqueues work on `stream` and returns; nothing is synchronised, nothing is
  *    allocated, and the library keeps no mutable global state, so calls on
  *    different streams may run concurrently. The caller owns every buffer.
+ *    The one exception is bitlinear_forward_noalloc, which uses a
+ *    library-owned scratch array per device (see there).
  *  - Outputs must not alias inputs. Device pointers must be 16-byte aligned.
  *  - Packed weight layout: row-major [n][k/4] bytes; byte j of a row holds the
  *    weights k = 4j+i in bits 2i..2i+1 (i = 0..3) as the code w+1 in {0,1,2};
@@ -175,6 +177,25 @@ bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden
                         const uint8_t *down_packed, const float *down_gamma,
                         float *y, int8_t *hq_out, float *hs_out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * bitlinear_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc. Same
+ * arguments and results as bitlinear_forward without the workspace: the
+ * scratch space comes from a library-owned device array of
+ * BL_NOALLOC_SCRATCH_BYTES per device, which each device the library runs on
+ * holds until the process ends. Nothing is allocated, freed or synchronised.
+ *   Returns BL_ERR_WORKSPACE when bitlinear_workspace_size(BL_OP_FORWARD, m, k, n)
+ *   exceeds BL_NOALLOC_SCRATCH_BYTES (e.g. m * roundup(k, 64) above ~32 M);
+ *   BL_ERR_VALUE when `stream` belongs to another device than the current one.
+ * Every call on a device shares that device's array, and the array keeps the
+ * last call's contents (every call writes what it reads first): calls that
+ * overlap on one device race -- serialise them (one stream, or events).
+ */
+#define BL_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+bl_status bitlinear_forward_noalloc(const void *x, bl_dtype dtype, int64_t m, int64_t k,
+                                    const uint8_t *packed, const float *gamma, int64_t n,
+                                    float *y, int32_t *acc_out, void *stream);
 
 /*
  * The bare ternary x int8 contraction ("穿越1比特的奇幻旅程", section

@@ -129,6 +129,20 @@ def test_other_entry_points_argument_errors(lib):
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, A, A, A, None, None, A, 16, None) == BL_ERR_WORKSPACE
 
 
+def test_noalloc_argument_errors(lib):
+    """The variant without a workspace rejects bad arguments, and sizes whose
+    scratch would exceed its 32 MiB array, before touching the device."""
+    f = lib.bitlinear_forward_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 1, 64, 256, A, A, 8, A, None, None) == BL_ERR_NULL
+    assert f(A, 9, 64, 256, A, A, 8, A, None, None) == BL_ERR_DTYPE
+    assert f(A, 1, 64, 258, A, A, 8, A, None, None) == BL_ERR_SHAPE
+    assert f(A, 1, 64, 256, MIS, A, 8, A, None, None) == BL_ERR_ALIGN
+    assert lib.bitlinear_workspace_size(OP_FORWARD, 4096, 8192, 64) > 32 << 20
+    assert f(A, 1, 4096, 8192, A, A, 64, A, None, None) == BL_ERR_WORKSPACE
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     """No CPU fallback: with the shared library absent, every call raises."""
     import bit_ternary_weight_bitlinear_amd as bl
