@@ -4,30 +4,39 @@
 Headline (the JSON line's `value`): decode, 1 token through the 2B-class FFN up
 (2560 -> 6912) and down (6912 -> 2560) BitLinear layers. One step = the whole
 hot path for that token: per-token int8 quantization (fused into the decode
-kernel's prologue), ternary x int8 product, rescale -- for both matrices. The
-packed weights rotate through a pool of distinct copies larger than 2x the
-256 MB last-level cache, so every step reads its weights from HBM.
+kernel's prologue), ternary x int8 product, rescale -- for both matrices.
 value = packed-weight bytes per step / step time (GB/s).
 
-Secondary (`prefill`, always measured): 2048 tokens through the same two
-layers on the int8 MFMA path; TOPS = 2*M*N*K per layer / step time.
-`--workload all` adds the batched-decode layer (m = 1, 8, 32, 64) and the
-8B-class FFN block (m = 1, 2048) under "extra".
+Every other workload is measured in the same run and reported under "extra":
+the small M=4, 256x256 layer (latency), one 2B-class layer at 1/8/32/64 tokens
+(packed GB/s), prefill at 2048 tokens through the two FFN matrices (int8
+TOPS), and the 8B-class FFN block at 1 and 2048 tokens.
 
-Timing: HIP events on the stream the kernels run on. `roofline` uses the
-dominant kernel's average launch duration: a graph of launches of that kernel
-alone (one matrix at a time, the same weight pool), timed over K launches.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Cold weights: the packed matrices of the HBM-bound workloads rotate through a
+pool of distinct copies larger than 2x the 256 MB last-level cache, and before
+every timed region 1 GiB of unrelated memory is streamed through the caches,
+so whatever --steps is, each timed step reads its weights from HBM.
 
-`--profile decode|prefill|layer8|ffn1|ffn2048` runs one workload eagerly (no graph
-capture, no JSON line) for profilers: `--steps` steps, then one plain device
-copy of 256 MiB whose HBM byte counters calibrate those of the kernels.
-layer8 is the batched-decode layer at 8 tokens, ffn1 / ffn2048 the 8B FFN at
-one / 2048 tokens.
+Timing: steps are captured in HIP graphs (no host launch overhead) and timed
+with HIP events on the stream the library launches on (torch's current
+stream). The headline times exactly --steps steps after --warmup eager ones.
+`roofline` is for the dominant kernel of the headline, the decode GEMV: its
+average launch duration comes from graphs of that kernel alone over the pool
+(events, this run); the figure from the committed rocprofv3 kernel trace is
+reported beside it while the kernel's sources match the ones traced. `read`
+is the plain streaming read of the same cold matrices (the achievable
+ceiling): once with the GEMV's grid and access pattern, once with the best
+grid found. `cpu_baseline` times the CPU oracle on bounded samples of every
+workload.
+
+`--profile decode|prefill|layer8|layer64|ffn1|ffn2048` runs one workload
+eagerly (no graphs, no JSON line) for profilers: --steps steps, then one plain
+256 MiB device copy whose HBM byte counters calibrate those of the kernels.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -48,9 +57,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 METRIC = "W1.58A8 BitLinear: decode GB/s vs HBM peak; prefill int8 TOPS vs MFMA peak"
 
-
-DECODE_COUNTERS = os.path.join("profiles", "gemv_decode_m1_2560x6912_6912x2560.md")
+DECODE_PROFILE = os.path.join("profiles", "gemv_decode_m1_2560x6912_6912x2560.md")
 DECODE_SOURCES = [os.path.join("bit_ternary_weight_bitlinear_amd", "csrc", f) for f in ("gemv.hip", "common.hpp")]
+FLUSH_BYTES = 512 << 20        # each of the two flush buffers; a flush moves 1 GiB
 
 
 def log(*a):
@@ -68,68 +77,113 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-# --------------------------------------------------------------------------- helpers
+def r4(v):
+    return None if v is None else round(float(v), 4)
+
+
+# --------------------------------------------------------------------------- timing
 
 class Timer:
-    """Times work on torch's current stream (the stream the library launches on)
-    with HIP events. Steps are captured into a HIP graph first, so the host's
-    launch overhead is not part of the measurement; the graph is replayed."""
+    """Times graph replays with HIP events on torch's current stream (the stream
+    the library launches on). `flush` streams 1 GiB of unrelated memory through
+    the caches before each timed region."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, dev):
         self.torch = torch
+        self.src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
 
-    def capture(self, fn, n):
+    def flush(self):
+        self.dst.copy_(self.src)
+
+    def capture(self, fn, n, start=0):
         t = self.torch
         g = t.cuda.CUDAGraph()
         side = t.cuda.Stream()
         side.wait_stream(t.cuda.current_stream())
         with t.cuda.stream(side):
-            fn(0)  # one eager call on the capture stream before capturing
+            fn(start)  # one eager call on the capture stream before capturing
         t.cuda.current_stream().wait_stream(side)
         with t.cuda.graph(g):
             for i in range(n):
-                fn(i)
+                fn(start + i)
         t.cuda.synchronize()
         return g
 
-    def graph_region(self, fn, steps, per_graph):
-        """Times exactly `steps` steps: a graph of `per_graph` steps (one cycle
-        of the weight pool) replayed steps // per_graph times, then a graph of
-        the remaining steps. Returns (seconds per step, steps done)."""
+    def _events(self, body):
         t = self.torch
-        steps = max(1, steps)
-        reps, rest = divmod(steps, per_graph)
-        g = self.capture(fn, per_graph) if reps else None
-        g_rest = self.capture(fn, rest) if rest else None
-        for gr in (g, g_rest):  # warm replays
-            if gr is not None:
-                gr.replay()
-        t.cuda.synchronize()
         st = t.cuda.current_stream()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         a.record(st)
-        for _ in range(reps):
-            g.replay()
-        if g_rest is not None:
-            g_rest.replay()
+        body()
         b.record(st)
         t.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3 / steps, steps
+        return a.elapsed_time(b) / 1e3
+
+    def steps_region(self, fn, steps, cycle):
+        """Exactly `steps` steps: a graph of one pool cycle replayed steps // cycle
+        times, then a graph of the remaining steps. Each graph is replayed once
+        untimed, then the caches are flushed. Returns seconds per step."""
+        steps = max(1, steps)
+        reps, rest = divmod(steps, cycle)
+        g = self.capture(fn, cycle) if reps else None
+        g_rest = self.capture(fn, rest) if rest else None
+        for gr in (g, g_rest):
+            if gr is not None:
+                gr.replay()
+        self.flush()
+
+        def body():
+            for _ in range(reps):
+                g.replay()
+            if g_rest is not None:
+                g_rest.replay()
+        return self._events(body) / steps
+
+    def launch_mean(self, fn, cycle, seconds=0.3):
+        """Mean time per call of `fn` from a graph of `cycle` calls (one pool
+        cycle) replayed for about `seconds`, after an untimed replay and a flush."""
+        g = self.capture(fn, cycle)
+        g.replay()
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        self.torch.cuda.synchronize()
+        per = max(time.perf_counter() - t0, 1e-6)
+        reps = int(min(5000, max(3, seconds / per)))
+        self.flush()
+        return self._events(lambda: [g.replay() for _ in range(reps)]) / (reps * cycle)
+
+
+# --------------------------------------------------------------------------- inputs
+
+_WEIGHTS = {}
+
+
+def weights(cfg, tid, n, k):
+    """Seeded fp32 weights, generated once per run and shared by the GPU legs and
+    the CPU baseline (each side quantizes them itself)."""
+    key = (cfg, tid, n, k)
+    if key not in _WEIGHTS:
+        _WEIGHTS[key] = synth.weights(cfg, tid, n, k)
+    return _WEIGHTS[key]
 
 
 def make_weights(bl, torch, cfg, tid, n, k, dev):
-    w = torch.from_numpy(synth.weights(cfg, tid, n, k)).to(dev)
+    w = torch.from_numpy(weights(cfg, tid, n, k)).to(dev)
     packed, gamma = bl.pack_weights(w)
     del w
     return packed, gamma
 
 
-def act_tensor(torch, cfg, m, k, dev, **kw):
-    xb = synth.activations(cfg, m, k, dtype="bf16", **kw)
-    return torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+def act_tensor(torch, cfg, m, k, dev, dtype="bf16", **kw):
+    x = synth.activations(cfg, m, k, dtype=dtype, **kw)
+    if dtype == "f32":
+        return torch.from_numpy(x).to(dev)
+    return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def rotation_pool(torch, mats, pool_bytes):
+def rotation_pool(mats, pool_bytes):
     """Distinct device copies of the packed matrices, cycled per step."""
     per = sum(p.numel() for p, _ in mats)
     copies = max(2, int(np.ceil(pool_bytes / per)))
@@ -137,66 +191,134 @@ def rotation_pool(torch, mats, pool_bytes):
     return pool, copies * per
 
 
-def counter_traffic():
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary (each counter scaled by what it reads for a
-    plain copy of known size), or None when the kernel's sources differ from
-    the ones the counters were taken with."""
-    try:
-        with open(os.path.join(ROOT, DECODE_COUNTERS)) as f:
-            text = f.read()
-    except OSError:
-        return None
-    fields = dict(re.findall(r"^(traffic_bytes_per_launch|source-sha256): (\S+)$", text, re.M))
-    h = hashlib.sha256()
-    for src in DECODE_SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if fields.get("source-sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
-        return None
-    return int(fields["traffic_bytes_per_launch"])
-
-
-# --------------------------------------------------------------------------- workloads
-
-def bench_decode(bl, torch, dev, steps, warmup, pool_mb):
+def decode_inputs(bl, torch, dev):
     cfg = synth.WORKLOADS[2]
-    mats, xs, ys = [], [], []
+    mats, xs = [], []
     for tid, (k, n) in zip(("up", "down"), cfg["mats"]):
         mats.append(make_weights(bl, torch, 2, tid, n, k, dev))
         xs.append(act_tensor(torch, 2, 1, k, dev, outlier_channels=round(0.01 * k),
                              outlier_scale=cfg["outlier_scale"]))
-        ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
-    pool, pool_bytes = rotation_pool(torch, mats, pool_mb << 20)
+    return cfg, mats, xs
+
+
+def profile_fields():
+    """Machine-readable fields of the committed decode profile, and whether the
+    decode kernel's sources still hash to the ones that were profiled."""
+    try:
+        with open(os.path.join(ROOT, DECODE_PROFILE)) as f:
+            text = f.read()
+    except OSError:
+        return {}, False
+    fields = dict(re.findall(r"^([a-z0-9_-]+): (.+)$", text, re.M))
+    h = hashlib.sha256()
+    for src in DECODE_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return fields, fields.get("source-sha256") == h.hexdigest()
+
+
+class ReadLib:
+    """The plain streaming-read kernels of libbitlinear_bench.so."""
+
+    def __init__(self, bl, torch, dev):
+        path = os.path.join(os.path.dirname(bl.library_path()), "libbitlinear_bench.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        i64, p, ci, cu = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
+        self.lib.blbench_read_rows.argtypes = [p, i64, i64, ci, ci, cu, p, p]
+        self.lib.blbench_read_linear.argtypes = [p, i64, ci, ci, cu, p, p]
+        self.sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+        self.torch = torch
+
+    def rows(self, packed, grid, threads):
+        n, ldw = packed.shape
+        rc = self.lib.blbench_read_rows(packed.data_ptr(), n, ldw, grid, threads, 0x9E3779B9,
+                                        self.sink.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"blbench_read_rows: {rc}")
+
+    def linear(self, packed, grid, threads):
+        rc = self.lib.blbench_read_linear(packed.data_ptr(), packed.numel(), grid, threads, 0x9E3779B9,
+                                          self.sink.data_ptr(), self.torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"blbench_read_linear: {rc}")
+
+
+# --------------------------------------------------------------------------- workloads
+
+def bench_decode(bl, torch, dev, tm, steps, warmup, pool_mb):
+    cfg, mats, xs = decode_inputs(bl, torch, dev)
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
+    pool, pool_bytes = rotation_pool(mats, pool_mb << 20)
+    P = len(pool)
     packed_bytes = sum(p.numel() for p, _ in mats)
     algo_bytes = [p.numel() + x.numel() * 2 + y.numel() * 4 for (p, _), x, y in zip(mats, xs, ys)]
 
     def step(i):
-        ws = pool[i % len(pool)]
+        ws = pool[i % P]
         for j in range(2):
             bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
 
     for i in range(warmup):
-        step(i)
-    tm = Timer(torch)
-    t_step, done = tm.graph_region(step, steps, len(pool))
-    # the dominant kernel alone, per shape: a graph of launches of one matrix, cycling the pool
-    per_shape = []
+        step(P - 1 - (i % P))
+    t_step = tm.steps_region(step, steps, P)
+
+    # the dominant kernel alone, per shape, and the plain reads of the same matrices
+    rd = ReadLib(bl, torch, dev)
+    per_shape, read_rows, read_lin = [], [], []
     for j in range(2):
-        def one(i, j=j):
-            ws = pool[i % len(pool)]
-            bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
-        tl, _ = tm.graph_region(one, steps, len(pool))
-        per_shape.append(tl)
-    res = dict(ms_per_step=t_step * 1e3, steps_done=done, packed_bytes_per_step=packed_bytes,
-               gbs=packed_bytes / t_step / 1e9,
-               kernel_mean_s=float(np.mean(per_shape)), kernel_per_shape_s=per_shape,
-               algo_bytes_per_launch=float(np.mean(algo_bytes)),
-               pool_bytes=pool_bytes, shapes=cfg["mats"])
-    return res, (mats, xs)
+        per_shape.append(tm.launch_mean(lambda i, j=j: bl.forward(xs[j], pool[i % P][j][0], pool[i % P][j][1],
+                                                                   out=ys[j]), P))
+        read_rows.append(tm.launch_mean(lambda i, j=j: rd.rows(pool[i % P][j][0], 256, 512), P))
+        read_lin.append(tm.launch_mean(lambda i, j=j: rd.linear(pool[i % P][j][0], 1024, 256), P))
+    return dict(ms_per_step=t_step * 1e3, steps=steps, packed_bytes_per_step=packed_bytes,
+                gbs=packed_bytes / t_step / 1e9, kernel_s=per_shape, algo_bytes=algo_bytes,
+                read_rows_s=read_rows, read_linear_s=read_lin, pool_bytes=pool_bytes, shapes=cfg["mats"])
 
 
-def bench_prefill(bl, torch, dev, steps, warmup):
+def bench_small(bl, torch, dev, tm):
+    cfg = synth.WORKLOADS[1]
+    m, k, n = cfg["m"], cfg["k"], cfg["n"]
+    packed, gamma = make_weights(bl, torch, 1, "W", n, k, dev)
+    x = act_tensor(torch, 1, m, k, dev, dtype="f32", outlier_channels=cfg["outliers"],
+                   outlier_scale=cfg["outlier_scale"])
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    t = tm.launch_mean(lambda i: bl.forward(x, packed, gamma, out=y), 100, seconds=0.1)
+    return dict(workload="M=4, K=N=256, fp32 activations (2 channels x20)", us_per_forward=round(t * 1e6, 3))
+
+
+def bench_layer(bl, torch, dev, tm, steps, warmup, pool_mb):
+    cfg = synth.WORKLOADS[3]
+    mats = [make_weights(bl, torch, 3, tid, n, k, dev)
+            for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), cfg["mats"])]
+    pool, pool_bytes = rotation_pool(mats, pool_mb << 20)
+    P = len(pool)
+    packed_bytes = sum(p.numel() for p, _ in mats)
+    out = dict(workload="one 2B-class layer: QKV 2560->3840, O 2560->2560, gate/up 2560->6912, "
+                        "down 6912->2560, bf16 activations, weights cold from HBM",
+               packed_bytes_per_layer=packed_bytes, pool_bytes=pool_bytes)
+    for m in cfg["ms"]:
+        xs = [act_tensor(torch, 3, m, k, dev) for k, _ in cfg["mats"]]
+        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
+        wss = [torch.empty(max(1, bl.workspace_size(bl.OP_FORWARD, m, k, n)), dtype=torch.uint8, device=dev)
+               for k, n in cfg["mats"]]
+
+        def step(i):
+            ws = pool[i % P]
+            for j in range(len(mats)):
+                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j],
+                           workspace=wss[j] if wss[j].numel() > 1 else None)
+
+        for i in range(warmup):
+            step(P - 1 - (i % P))
+        t = tm.steps_region(step, steps, P)
+        out[f"m{m}"] = dict(us_per_layer=round(t * 1e6, 3), packed_gbs=round(packed_bytes / t / 1e9, 2),
+                            frac_of_hbm_peak=r4(packed_bytes / t / 1e9 / HBM_PEAK_GBS))
+    return out
+
+
+def bench_prefill(bl, torch, dev, tm, steps, warmup):
     cfg = synth.WORKLOADS[4]
     m = cfg["m"]
     mats, xs, ys, wss = [], [], [], []
@@ -206,57 +328,35 @@ def bench_prefill(bl, torch, dev, steps, warmup):
         ys.append(torch.empty((m, n), dtype=torch.float32, device=dev))
         wss.append(torch.empty(bl.workspace_size(bl.OP_FORWARD, m, k, n), dtype=torch.uint8, device=dev))
 
-    def step(i):
-        for j in range(2):
-            bl.forward(xs[j], mats[j][0], mats[j][1], out=ys[j], workspace=wss[j])
+    def one(j):
+        bl.forward(xs[j], mats[j][0], mats[j][1], out=ys[j], workspace=wss[j])
 
-    for i in range(warmup):
-        step(i)
-    t, _ = Timer(torch).graph_region(step, steps, min(steps, 8))
-    ops = sum(2.0 * m * n * k for k, n in cfg["mats"])
-    return dict(ms_per_step=t * 1e3, tops=ops / t / 1e12, ops_per_step=ops,
-                frac_of_mfma_peak=ops / t / 1e12 / INT8_MFMA_PEAK_TOPS, m=m, shapes=cfg["mats"])
-
-
-def bench_layer(bl, torch, dev, steps, warmup, pool_mb):
-    cfg = synth.WORKLOADS[3]
-    mats = [make_weights(bl, torch, 3, tid, n, k, dev)
-            for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), cfg["mats"])]
-    pool, pool_bytes = rotation_pool(torch, mats, pool_mb << 20)
-    packed_bytes = sum(p.numel() for p, _ in mats)
-    out = {}
-    for m in cfg["ms"]:
-        xs = [act_tensor(torch, 3, m, k, dev) for k, _ in cfg["mats"]]
-        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
-        wss = [torch.empty(max(1, bl.workspace_size(bl.OP_FORWARD, m, k, n)), dtype=torch.uint8, device=dev)
-               for k, n in cfg["mats"]]
-
-        def step(i):
-            ws = pool[i % len(pool)]
-            for j in range(len(mats)):
-                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j], workspace=wss[j])
-
-        for i in range(warmup):
-            step(i)
-        t, _ = Timer(torch).graph_region(step, steps, len(pool))
-        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9,
-                            frac_of_hbm_peak=packed_bytes / t / 1e9 / HBM_PEAK_GBS)
-    out["packed_bytes_per_layer"] = packed_bytes
-    out["pool_bytes"] = pool_bytes
-    return out
+    for _ in range(warmup):
+        one(0)
+        one(1)
+    t = tm.steps_region(lambda i: (one(0), one(1)), steps, min(steps, 8))
+    per = [tm.launch_mean(lambda i, j=j: one(j), 8, seconds=0.2) for j in range(2)]
+    ops = [2.0 * m * n * k for k, n in cfg["mats"]]
+    return dict(workload="prefill m=2048: 2560->6912 + 6912->2560, bf16 activations (1% Student-t channels), "
+                         "act-quant + GEMM per layer",
+                ms_per_step=round(t * 1e3, 4), tops=round(sum(ops) / t / 1e12, 2),
+                frac_of_int8_mfma_peak=r4(sum(ops) / t / 1e12 / INT8_MFMA_PEAK_TOPS),
+                per_layer_us=[round(v * 1e6, 2) for v in per],
+                per_layer_tops=[round(o / v / 1e12, 1) for o, v in zip(ops, per)])
 
 
-def bench_ffn(bl, torch, dev, steps, warmup, pool_mb):
+def bench_ffn(bl, torch, dev, tm, steps, warmup, pool_mb):
     cfg = synth.WORKLOADS[5]
     hid, f = cfg["hidden"], cfg["ffn"]
     mats = [make_weights(bl, torch, 5, "gate", f, hid, dev), make_weights(bl, torch, 5, "up", f, hid, dev),
             make_weights(bl, torch, 5, "down", hid, f, dev)]
     packed_bytes = 3 * f * hid // 4
-    out = {}
+    out = dict(workload="8B-class FFN block: gate+up 4096->14336, relu(g)^2*u, requant, down 14336->4096",
+               packed_bytes=packed_bytes)
     for m in cfg["ms"]:
-        # one token: the weights rotate through distinct copies (cold from HBM,
-        # as for decode); 2048 tokens: compute-bound, one copy
-        pool, pool_bytes = rotation_pool(torch, mats, pool_mb << 20) if m == 1 else ([mats], packed_bytes)
+        # one token: weights cold from a rotation pool (HBM-bound); 2048 tokens:
+        # compute-bound, one copy
+        pool, pool_bytes = rotation_pool(mats, pool_mb << 20) if m == 1 else ([mats], packed_bytes)
         x = act_tensor(torch, 5, m, hid, dev)
         ws = torch.empty(bl.workspace_size(bl.OP_FFN, m, hid, f), dtype=torch.uint8, device=dev)
 
@@ -265,37 +365,45 @@ def bench_ffn(bl, torch, dev, steps, warmup, pool_mb):
             bl.ffn(x, g, u, d, workspace=ws)
 
         for i in range(warmup):
-            step(i)
-        t, _ = Timer(torch).graph_region(step, steps, len(pool) if m == 1 else min(steps, 8))
+            step(len(pool) - 1 - (i % len(pool)))
+        t = tm.steps_region(step, steps, len(pool) if m == 1 else min(steps, 8))
         ops = 2.0 * m * 3 * f * hid
-        out[f"m{m}"] = dict(ms_per_step=t * 1e3, packed_gbs=packed_bytes / t / 1e9, tops=ops / t / 1e12,
-                            pool_bytes=pool_bytes)
+        if m == 1:
+            out["m1"] = dict(us_per_ffn=round(t * 1e6, 3), packed_gbs=round(packed_bytes / t / 1e9, 2),
+                             frac_of_hbm_peak=r4(packed_bytes / t / 1e9 / HBM_PEAK_GBS), pool_bytes=pool_bytes)
+        else:
+            out[f"m{m}"] = dict(ms_per_ffn=round(t * 1e3, 4), tops=round(ops / t / 1e12, 2),
+                                frac_of_int8_mfma_peak=r4(ops / t / 1e12 / INT8_MFMA_PEAK_TOPS))
         del pool
     return out
 
 
+# --------------------------------------------------------------------------- profiling
+
 def profile_run(bl, torch, dev, what, steps, pool_mb):
     """Eager launches of one workload for rocprofv3, then a 256 MiB copy."""
     if what == "decode":
-        cfg = synth.WORKLOADS[2]
-        mats, xs, ys = [], [], []
-        for tid, (k, n) in zip(("up", "down"), cfg["mats"]):
-            mats.append(make_weights(bl, torch, 2, tid, n, k, dev))
-            xs.append(act_tensor(torch, 2, 1, k, dev, outlier_channels=round(0.01 * k),
-                                 outlier_scale=cfg["outlier_scale"]))
-            ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
-        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        cfg, mats, xs = decode_inputs(bl, torch, dev)
+        ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
+        pool, _ = rotation_pool(mats, pool_mb << 20)
+        rd = ReadLib(bl, torch, dev)
         for i in range(steps):
             ws = pool[i % len(pool)]
             for j in range(2):
                 bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j])
-    elif what == "layer8":
-        # the 2B-class layer at 8 tokens, weights cold from the rotation pool
+        # the plain reads of the same cold matrices (GEMV grid and pattern, then linear)
+        for i in range(steps):
+            for j in range(2):
+                rd.rows(pool[(i + steps) % len(pool)][j][0], 256, 512)
+        for i in range(steps):
+            for j in range(2):
+                rd.linear(pool[(i + 2 * steps) % len(pool)][j][0], 1024, 256)
+    elif what in ("layer8", "layer64"):
         cfg = synth.WORKLOADS[3]
-        m = 8
+        m = 8 if what == "layer8" else 64
         mats = [make_weights(bl, torch, 3, tid, n, k, dev)
                 for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), cfg["mats"])]
-        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        pool, _ = rotation_pool(mats, pool_mb << 20)
         xs = [act_tensor(torch, 3, m, k, dev) for k, _ in cfg["mats"]]
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
         wss = [torch.empty(max(1, bl.workspace_size(bl.OP_FORWARD, m, k, n)), dtype=torch.uint8, device=dev)
@@ -303,21 +411,19 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
         for i in range(steps):
             ws = pool[i % len(pool)]
             for j in range(len(mats)):
-                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j], workspace=wss[j])
+                bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j], workspace=wss[j] if wss[j].numel() > 1 else None)
     elif what == "ffn1":
-        # the 8B-class FFN block at one token, weights cold from the rotation pool
         cfg = synth.WORKLOADS[5]
         hid, f = cfg["hidden"], cfg["ffn"]
         mats = [make_weights(bl, torch, 5, "gate", f, hid, dev), make_weights(bl, torch, 5, "up", f, hid, dev),
                 make_weights(bl, torch, 5, "down", hid, f, dev)]
-        pool, _ = rotation_pool(torch, mats, pool_mb << 20)
+        pool, _ = rotation_pool(mats, pool_mb << 20)
         x = act_tensor(torch, 5, 1, hid, dev)
         ws = torch.empty(bl.workspace_size(bl.OP_FFN, 1, hid, f), dtype=torch.uint8, device=dev)
         for i in range(steps):
             g, u, d = pool[i % len(pool)]
             bl.ffn(x, g, u, d, workspace=ws)
     elif what == "ffn2048":
-        # the 8B-class FFN block at 2048 tokens (compute-bound: one copy of the weights)
         cfg = synth.WORKLOADS[5]
         hid, f, m = cfg["hidden"], cfg["ffn"], max(cfg["ms"])
         g = make_weights(bl, torch, 5, "gate", f, hid, dev)
@@ -346,30 +452,103 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The CPU oracle on a bounded sample of the decode workload: whole steps
-    (both matrices, one token each) until ~budget_s of CPU time is used."""
+def _median_time(fn, reps=3):
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline():
+    """The CPU oracle, as it stands, on bounded samples of every workload: the
+    median of 3 runs with all host threads (OpenMP over output rows), and for
+    the small, decode and batched-decode workloads also with one thread. Large
+    token counts are sampled (the rate per operation does not depend on how
+    many tokens there are); each entry says what it ran."""
     import oracle
-    cfg = synth.WORKLOADS[2]
-    mats, xs = [], []
-    for tid, (k, n) in zip(("up", "down"), cfg["mats"]):
-        w = synth.weights(2, tid, n, k)
-        p, g, _ = oracle.pack_weights(w)
-        mats.append((p, g, k))
-        xs.append(synth.activations(2, 1, k, dtype="bf16", outlier_channels=round(0.01 * k),
-                                    outlier_scale=cfg["outlier_scale"]))
-    packed_bytes = sum(p.size for p, _, _ in mats)
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for (p, g, k), x in zip(mats, xs):
-            oracle.forward(x, p, g, k, "bf16")
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 10000:
-            break
-    return dict(value=packed_bytes * steps / el / 1e9, unit="GB/s", cores=oracle.num_threads(),
-                kind="oracle", sample=f"{steps} decode steps (1 token through 2560->6912 and 6912->2560) "
-                                      f"in {el:.1f} s; CPU: {cpu_model()}, {os.cpu_count()} logical cores")
+    nthreads = oracle.num_threads()
+    out = {}
+
+    def layer(cfg, tid, k, n, m, **act):
+        p, g, _ = oracle.pack_weights(weights(cfg, tid, n, k))
+        x = synth.activations(cfg, m, k, **act)
+        return p, g, x
+
+    def timed(run, threads):
+        oracle.set_num_threads(threads)
+        try:
+            return _median_time(run)
+        finally:
+            oracle.set_num_threads(nthreads)
+
+    # 1: m=4, 256x256, fp32 activations
+    c1 = synth.WORKLOADS[1]
+    p, g, x = layer(1, "W", c1["k"], c1["n"], c1["m"], dtype="f32", outlier_channels=2, outlier_scale=20.0)
+    run = lambda: oracle.forward(x, p, g, c1["k"], "f32")  # noqa: E731
+    out["small_m4_256x256"] = dict(us_all_threads=round(timed(run, nthreads) * 1e6, 1),
+                                   us_1_thread=round(timed(run, 1) * 1e6, 1))
+
+    # 2: decode, both matrices, one token
+    c2 = synth.WORKLOADS[2]
+    dec = [layer(2, tid, k, n, 1, outlier_channels=round(0.01 * k), outlier_scale=c2["outlier_scale"])
+           for tid, (k, n) in zip(("up", "down"), c2["mats"])]
+    dec_bytes = sum(p.size for p, _, _ in dec)
+    run = lambda: [oracle.forward(x, p, g, x.shape[1], "bf16") for p, g, x in dec]  # noqa: E731
+    t_all, t_one = timed(run, nthreads), timed(run, 1)
+    out["decode_m1"] = dict(gbs_all_threads=round(dec_bytes / t_all / 1e9, 4),
+                            gbs_1_thread=round(dec_bytes / t_one / 1e9, 4), us_per_step=round(t_all * 1e6, 1))
+    headline = dec_bytes / t_all / 1e9
+
+    # 3: one 2B-class layer; one thread at 1 and 8 tokens only (bounded)
+    c3 = synth.WORKLOADS[3]
+    lay = [(tid, k, n, oracle.pack_weights(weights(3, tid, n, k))[:2])
+           for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), c3["mats"])]
+    lay_bytes = sum(pg[0].size for _, _, _, pg in lay)
+    res3 = {}
+    for m in c3["ms"]:
+        xs = [synth.activations(3, m, k) for _, k, _, _ in lay]
+        run = lambda xs=xs: [oracle.forward(x, pg[0], pg[1], k, "bf16")  # noqa: E731
+                             for x, (_, k, _, pg) in zip(xs, lay)]
+        e = dict(gbs_all_threads=round(lay_bytes / timed(run, nthreads) / 1e9, 4))
+        if m <= 8:
+            e["gbs_1_thread"] = round(lay_bytes / timed(run, 1) / 1e9, 4)
+        res3[f"m{m}"] = e
+    out["layer_2b"] = res3
+
+    # 4: prefill, 128 of the 2048 tokens through both matrices (int8 TOPS)
+    c4 = synth.WORKLOADS[4]
+    ms = 128
+    pre = []
+    for tid, (k, n) in zip(("up", "down"), c4["mats"]):
+        p, g, x = layer(4, tid, k, n, c4["m"], heavy_channels=round(0.01 * k))
+        pre.append((p, g, x[:ms], k, n))
+    run = lambda: [oracle.forward(x, p, g, k, "bf16") for p, g, x, k, _ in pre]  # noqa: E731
+    ops = sum(2.0 * ms * n * k for _, _, _, k, n in pre)
+    out["prefill_m2048"] = dict(tops_all_threads=round(ops / timed(run, nthreads) / 1e12, 5),
+                                sample="128 of the 2048 tokens")
+
+    # 5: 8B FFN at one token (GB/s) and 32 of the 2048 tokens (TOPS, one run)
+    c5 = synth.WORKLOADS[5]
+    hid, f = c5["hidden"], c5["ffn"]
+    ws_ = {nm: oracle.pack_weights(weights(5, nm, *sh))[:2]
+           for nm, sh in (("gate", (f, hid)), ("up", (f, hid)), ("down", (hid, f)))}
+    x1 = synth.activations(5, 1, hid)
+    t1 = timed(lambda: oracle.ffn(x1, ws_["gate"], ws_["up"], ws_["down"], hid, f, "bf16"), nthreads)
+    xs = synth.activations(5, 2048, hid)[:32]
+    oracle.set_num_threads(nthreads)
+    t0 = time.perf_counter()
+    oracle.ffn(xs, ws_["gate"], ws_["up"], ws_["down"], hid, f, "bf16")
+    t32 = time.perf_counter() - t0
+    out["ffn_8b"] = dict(m1_gbs_all_threads=round(3 * f * hid / 4 / t1 / 1e9, 4),
+                         m2048_tops_all_threads=round(2.0 * 32 * 3 * f * hid / t32 / 1e12, 5),
+                         m2048_sample="32 of the 2048 tokens, one run")
+    return dict(value=round(headline, 4), unit="GB/s", cores=nthreads, kind="oracle",
+                sample=(f"decode: both matrices (1 token through 2560->6912 and 6912->2560), median of 3 runs "
+                        f"with {nthreads} OpenMP threads; per_config holds every workload (bounded samples "
+                        f"as stated) and one-thread runs; CPU: {cpu_model()}, {os.cpu_count()} logical cores"),
+                per_config=out)
 
 
 # --------------------------------------------------------------------------- main
@@ -380,14 +559,14 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
-    ap.add_argument("--workload", choices=["default", "all"], default="default")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "ffn1", "ffn2048"], default=None,
-                    help="eager launches for a profiler; prints no JSON line")
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn2048"],
+                    default=None, help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are not supported",
+        print("bench.py: this build measures one GPU only (--gpus 1); runs on several GPUs are not supported",
               file=sys.stderr)
         sys.exit(2)
 
@@ -400,28 +579,57 @@ def main():
         profile_run(bl, torch, dev, args.profile, args.steps, args.pool_mb)
         return
 
-    dec, _ = bench_decode(bl, torch, dev, args.steps, args.warmup, args.pool_mb)
-    log(f"decode: {dec['ms_per_step']*1e3:.2f} us/step, {dec['gbs']:.1f} GB/s packed, "
-        f"kernel {dec['kernel_mean_s']*1e6:.2f} us mean")
-    pre = bench_prefill(bl, torch, dev, max(10, args.steps // 10), max(3, args.warmup // 5))
-    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tops']:.1f} TOPS")
+    tm = Timer(torch, dev)
+    dec = bench_decode(bl, torch, dev, tm, args.steps, args.warmup, args.pool_mb)
+    log(f"decode: {dec['ms_per_step']*1e3:.2f} us/step, {dec['gbs']:.1f} GB/s packed; GEMV "
+        f"{[round(v * 1e6, 3) for v in dec['kernel_s']]} us, read (GEMV grid) "
+        f"{[round(v * 1e6, 3) for v in dec['read_rows_s']]} us, read (1024 wg) "
+        f"{[round(v * 1e6, 3) for v in dec['read_linear_s']]} us")
+    heavy_steps, heavy_warmup = max(10, args.steps // 10), max(3, args.warmup // 5)
     extra = {}
-    if args.workload == "all":
-        extra["batched_decode_layer"] = bench_layer(bl, torch, dev, args.steps, args.warmup, args.pool_mb)
+    if not args.headline_only:
+        extra["small"] = bench_small(bl, torch, dev, tm)
+        log("small:", json.dumps(extra["small"]))
+        extra["batched_decode_layer"] = bench_layer(bl, torch, dev, tm, args.steps, args.warmup, args.pool_mb)
         log("layer:", json.dumps(extra["batched_decode_layer"]))
-        extra["ffn_8b"] = bench_ffn(bl, torch, dev, max(10, args.steps // 10), max(3, args.warmup // 5), args.pool_mb)
+    prefill = bench_prefill(bl, torch, dev, tm, heavy_steps, heavy_warmup)
+    log("prefill:", json.dumps(prefill))
+    if not args.headline_only:
+        extra["ffn_8b"] = bench_ffn(bl, torch, dev, tm, heavy_steps, heavy_warmup, args.pool_mb)
         log("ffn:", json.dumps(extra["ffn_8b"]))
 
-    achieved = dec["algo_bytes_per_launch"] / dec["kernel_mean_s"] / 1e9
-    traffic = counter_traffic()
-    roofline = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    traffic_note=(f"HBM bytes per launch, {DECODE_COUNTERS}" if traffic else
-                                  "no counter summary for the current decode kernel sources"),
-                    kernel="gemv_kernel (decode, fused act-quant + v_dot4)",
-                    algo_bytes_per_launch=dec["algo_bytes_per_launch"],
-                    mean_launch_us=round(dec["kernel_mean_s"] * 1e6, 3),
-                    per_shape_launch_us=[round(v * 1e6, 3) for v in dec["kernel_per_shape_s"]])
+    algo = float(np.mean(dec["algo_bytes"]))
+    kmean = float(np.mean(dec["kernel_s"]))
+    achieved = algo / kmean / 1e9
+    fields, fresh = profile_fields()
+    trace_us = float(fields["trace_gemv_mean_us"]) if fresh and "trace_gemv_mean_us" in fields else None
+    traffic = int(fields["traffic_bytes_per_launch"]) if fresh and "traffic_bytes_per_launch" in fields else None
+    read_rows_us = [v * 1e6 for v in dec["read_rows_s"]]
+    read_lin_us = [v * 1e6 for v in dec["read_linear_s"]]
+    roofline = dict(
+        bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+        frac=r4(achieved / HBM_PEAK_GBS), traffic=traffic,
+        kernel="gemv_kernel (decode: act-quant fused, v_dot4 on packed ternary codes)",
+        algo_bytes_per_launch=algo,
+        mean_launch_us=round(kmean * 1e6, 3),
+        per_shape_launch_us=[round(v * 1e6, 3) for v in dec["kernel_s"]],
+        timing="HIP events over graphs of this kernel alone (one matrix per launch, weights cold), this run",
+        trace=(dict(mean_launch_us=trace_us, achieved=round(algo / (trace_us * 1e-6) / 1e9, 2),
+                    frac=r4(algo / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS),
+                    read_gemv_grid_us=float(fields["trace_read_rows_mean_us"]),
+                    read_best_grid_us=float(fields["trace_read_linear_mean_us"]),
+                    source=f"rocprofv3 kernel trace of the bench, {DECODE_PROFILE}") if trace_us else None),
+        traffic_note=(f"HBM bytes per launch from FETCH_SIZE/WRITE_SIZE, {DECODE_PROFILE}" if traffic else
+                      "no counter summary for the current decode kernel sources"),
+        read=dict(gemv_grid_us_per_shape=[round(v, 3) for v in read_rows_us],
+                  gemv_grid_gbs=round(sum(dec["shapes"][j][0] * dec["shapes"][j][1] / 4 for j in range(2)) /
+                                      (sum(read_rows_us) * 1e-6) / 1e9, 1),
+                  best_grid_us_per_shape=[round(v, 3) for v in read_lin_us],
+                  best_grid_gbs=round(sum(dec["shapes"][j][0] * dec["shapes"][j][1] / 4 for j in range(2)) /
+                                      (sum(read_lin_us) * 1e-6) / 1e9, 1),
+                  note="plain 16-byte non-temporal reads of the same cold packed matrices: 256 x 512 threads "
+                       "in the GEMV's pattern, and 1024 x 256 threads linear"),
+    )
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -429,27 +637,23 @@ def main():
         "value": round(dec["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": dec["steps_done"],
+        "steps": dec["steps"],
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xternary->int32 (bf16 in, fp32 out)",
+        "dtype": "int8 x ternary -> int32 (bf16 in, fp32 out)",
         "data": "synthetic",
         "config": {"workload": "decode GEMV m=1: 2B-class FFN up 2560->6912 + down 6912->2560, bf16 "
                                "activations (1% channels x30), packed weights cold from HBM",
                    "m": 1, "shapes_k_n": dec["shapes"], "packed_bytes_per_step": dec["packed_bytes_per_step"],
-                   "rotation_pool_bytes": dec["pool_bytes"]},
+                   "rotation_pool_bytes": dec["pool_bytes"], "cache_flush_bytes_before_timing": 2 * FLUSH_BYTES},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "prefill": {"workload": "prefill GEMM m=2048: 2560->6912 + 6912->2560, bf16 activations "
-                                "(1% Student-t channels)", "tops": round(pre["tops"], 2),
-                    "ms_per_step": round(pre["ms_per_step"], 4),
-                    "frac_of_int8_mfma_peak": round(pre["frac_of_mfma_peak"], 4)},
+        "prefill": prefill,
+        "extra": extra,
     }
-    if extra:
-        line["extra"] = extra
     print(json.dumps(line), flush=True)
 
 

@@ -1,4 +1,6 @@
-"""Compile the gfx950 HIP sources into bit_ternary_weight_bitlinear_amd/libbitlinear.so.
+"""Compile the gfx950 HIP sources into bit_ternary_weight_bitlinear_amd/libbitlinear.so
+(the product library) and libbitlinear_bench.so (the benchmark's plain read
+kernels, loaded by bench.py only).
 
 Flags: correctly rounded fp32 division, no FMA contraction, no fast-math, no
 denormal flushing (the quantizers decide integers in fp32 and must match the
@@ -14,7 +16,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
+BENCH_LIB = os.path.join(HERE, "libbitlinear_bench.so")
 SOURCES = ["api.hip", "pack.hip", "act_quant.hip", "gemv.hip", "bgemv.hip", "gemm.hip", "skinny.hip"]
+BENCH_SOURCES = ["bench_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -42,13 +46,15 @@ def build(verbose: bool = False, out_dir: str | None = None) -> str:
             print(r.stderr, flush=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    all_src = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(all_src), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(all_src, ex.map(compile_one, all_src)))
+    for lib, srcs in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[objs[s] for s in srcs], "-o", lib + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 
