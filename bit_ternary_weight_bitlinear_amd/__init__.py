@@ -9,6 +9,8 @@ Functions mirror the C entry points:
   pack_weights(w)                      -> (packed uint8 [n][k/4], gamma fp32 [1])
   pack_weights_threshold(w, factor)    -> (packed uint8 [n][k/4], alpha fp32 [1], delta fp32 [1])
   quant_act(x)                         -> (q int8 [m][k], scale fp32 [m])
+  quant_act_norm(x, gain=None)         -> the same for the RMS-normalized x
+  forward_norm(x, packed, gamma, gain=None) -> y fp32 [m][n] of the RMS-normalized x
   forward(x, packed, gamma)            -> y fp32 [m][n]        (return_acc=True adds acc)
   ffn(x, gate, up, down)               -> y fp32 [m][hidden]   (return_hq=True adds qh, sh)
   gemm_i32(q, packed)                  -> acc int32 [m][n]
@@ -22,14 +24,14 @@ import os
 
 import torch
 
-__all__ = ["pack_weights", "pack_weights_threshold", "quant_act", "forward", "ffn", "gemm_i32", "workspace_size",
+__all__ = ["pack_weights", "pack_weights_threshold", "quant_act", "quant_act_norm", "forward_norm", "forward", "ffn", "gemm_i32", "workspace_size",
            "library_path", "load_library", "BitLinearError", "OP_FORWARD", "OP_FFN", "OP_PACK",
-           "OP_GEMM_I32", "OP_PACK_THRESHOLD"]
+           "OP_GEMM_I32", "OP_PACK_THRESHOLD", "OP_FORWARD_NORM"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD = 0, 1, 2, 3, 4  # bl_op in include/bitlinear.h
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM = 0, 1, 2, 3, 4, 5  # bl_op
 _F32, _BF16 = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -44,6 +46,9 @@ _SIGNATURES = {
     "bitlinear_pack_weights_threshold": (_c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p,
                                                   _c_p, _c_size, _c_p]),
     "bitlinear_quant_act": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "bitlinear_quant_act_norm": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "bitlinear_forward_norm": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                        _c_p, _c_size, _c_p]),
     "bitlinear_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p,
                                    _c_p, _c_size, _c_p]),
     "bitlinear_ffn": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
@@ -179,6 +184,48 @@ def quant_act(x: torch.Tensor):
     _check(lib.bitlinear_quant_act(_dev(x, "x"), _act_dtype(x), m, k, q.data_ptr(), s.data_ptr(),
                                    _stream(x.device)), "bitlinear_quant_act")
     return q, s
+
+
+def _gain(gain, k: int):
+    if gain is None:
+        return None
+    if gain.numel() != k:
+        raise BitLinearError(f"gain must have {k} entries, got {gain.numel()}")
+    return _dev(gain, "gain", torch.float32)
+
+
+def quant_act_norm(x: torch.Tensor, gain: torch.Tensor | None = None):
+    """RMS-normalized activations [m][k] -> (q int8 [m][k], scale fp32 [m])."""
+    lib = load_library()
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    s = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(lib.bitlinear_quant_act_norm(_dev(x, "x"), _act_dtype(x), m, k, _gain(gain, k), q.data_ptr(),
+                                        s.data_ptr(), _stream(x.device)), "bitlinear_quant_act_norm")
+    return q, s
+
+
+def forward_norm(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, gain: torch.Tensor | None = None,
+                 *, return_acc: bool = False, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """BitLinear forward of the RMS-normalized x (the normalization fused into the quantization)."""
+    lib = load_library()
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 4 != k:
+        raise BitLinearError("packed weights do not match the activation width")
+    if out is not None:
+        _check_out(out, (m, n), torch.float32, "out")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if return_acc else None
+    ws = (_caller_workspace(workspace, OP_FORWARD_NORM, m, k, n) if workspace is not None
+          else _workspace(OP_FORWARD_NORM, m, k, n, x.device))
+    wp, wn = _ws_args(ws)
+    _check(lib.bitlinear_forward_norm(_dev(x, "x"), _act_dtype(x), m, k, _gain(gain, k),
+                                      _dev(packed, "packed", torch.uint8), _dev(gamma, "gamma", torch.float32), n,
+                                      _dev(y, "y", torch.float32), acc.data_ptr() if acc is not None else None,
+                                      wp, wn, _stream(x.device)), "bitlinear_forward_norm")
+    return (y, acc) if return_acc else y
 
 
 def forward(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, *, return_acc: bool = False,

@@ -13,6 +13,16 @@
 // rows keep few registers and many tokens are in flight per CU. The absmax and
 // the sum of the codes are reduced with DPP inside each wave and through LDS
 // across the four waves. HBM-bound: it reads the row once and writes k bytes.
+//
+// NORM: an RMS normalization runs first (subln: "穿越1比特的奇幻旅程", section
+// 架构创新; layer normalization with epsilon 1e-5: "BitNet 中使用直通估计器工程化
+// 三元权重训练", section 工程化训练流程与参数配置), and the absmax quantization
+// then applies to x^ = (x * r) * g, r = 1 / sqrt(fp32(S / k) + 1e-5), with
+// S = sum of x^2. Every square is exact in fp64; the sum is kept as a
+// double-double (TwoSum: each addition's rounding error is carried exactly),
+// so hi + lo rounds to the correctly rounded S unless S lies within about
+// k^2 2^-106 of a rounding boundary of fp64. The fp32 steps after it are
+// single correctly rounded operations (no contraction in this build).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,31 +56,143 @@ __device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const uint4 
         if (16 * g + 4 * j < k) p[j] = d[j];
 }
 
+// a + b = s + e exactly (Knuth's TwoSum)
+__device__ inline void two_sum(double a, double b, double &s, double &e)
+{
+    s = a + b;
+    const double bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+// double-double accumulation of one value
+__device__ inline void dd_add(double &hi, double &lo, double v)
+{
+    double e;
+    two_sum(hi, v, hi, e);
+    lo += e;
+}
+
+// double-double sum over the workgroup (xor butterfly in each wave, then the
+// four wave results in order through LDS); every thread gets the fp64 result
+__device__ inline double block_sum_dd(double hi, double lo, double *red)
+{
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        const double ph = __shfl_xor(hi, mask, 64);
+        const double pl = __shfl_xor(lo, mask, 64);
+        double e;
+        two_sum(hi, ph, hi, e);
+        lo = lo + pl + e;
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[2 * (threadIdx.x >> 6)] = hi;
+        red[2 * (threadIdx.x >> 6) + 1] = lo;
+    }
+    __syncthreads();
+    double h = red[0], l = red[1];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        double e;
+        two_sum(h, red[2 * w], h, e);
+        l = l + red[2 * w + 1] + e;
+    }
+    return h + l;
+}
+
+// the per-token factor r = 1 / sqrt(fp32(S / k) + 1e-5)
+__device__ inline float norm_factor(double ssq, int64_t k)
+{
+    const float ms = (float)(ssq / (double)k);
+    const float d = ms + kEps;
+    return 1.0f / sqrtf(d);
+}
+
+// x^ = (x * r) * g for the 16 inputs of group g (gain entries past k unused)
+template <bool GAIN>
+__device__ inline void normalize_group(float f[16], float r, const float *gain, int64_t k, int64_t g)
+{
+    const int64_t k0 = 16 * g;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) f[j] = f[j] * r;
+    if constexpr (GAIN) {
+        if (k0 + 16 <= k) {
+            const float4 *gp = reinterpret_cast<const float4 *>(gain + k0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 gv = gp[j];
+                f[4 * j + 0] = f[4 * j + 0] * gv.x;
+                f[4 * j + 1] = f[4 * j + 1] * gv.y;
+                f[4 * j + 2] = f[4 * j + 2] * gv.z;
+                f[4 * j + 3] = f[4 * j + 3] * gv.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) f[j] = (k0 + j < k) ? f[j] * gain[k0 + j] : 0.0f;
+        }
+    }
+}
+
 }  // namespace
 
 constexpr int kResidentGroups = 4;
 
-template <typename T, bool FULL, int RG>
+// NORM = 0: plain absmax quantization; 1: RMS norm first, no gain; 2: RMS norm
+// with the per-channel gain `gain` [k]
+template <typename T, bool FULL, int RG, int NORM = 0>
 __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x, int64_t k, int64_t kp,
                                                         int8_t *__restrict__ q_nat,
                                                         int8_t *__restrict__ q_perm,
-                                                        float *__restrict__ s, int32_t *__restrict__ sumq)
+                                                        float *__restrict__ s, int32_t *__restrict__ sumq,
+                                                        const float *__restrict__ gain)
 {
     __shared__ float red_f[4];
     __shared__ int red_i[4];
+    __shared__ double red_d[8];
     const int64_t t = blockIdx.x;
     const T *row = x + t * k;
     const int64_t G = ceil_div(k, 16);
     const bool resident = G <= (int64_t)RG * kThreads;
 
+    // a group as the quantizer sees it: the inputs, normalized when NORM is set
+    float r_norm = 1.0f;
+    auto load = [&](int64_t g, float f[16]) {
+        load_group<T, FULL>(row, k, g, f);
+        if constexpr (NORM != 0) normalize_group<NORM == 2>(f, r_norm, gain, k, g);
+    };
+
     float v[RG][16];
+    if constexpr (NORM != 0) {
+        double hi = 0.0, lo = 0.0;
+        auto sq = [&](const float f[16]) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) dd_add(hi, lo, (double)f[j] * (double)f[j]);
+        };
+        if (resident) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const int64_t g = threadIdx.x + r * kThreads;
+                if (g < G) {
+                    load_group<T, FULL>(row, k, g, v[r]);
+                    sq(v[r]);
+                }
+            }
+        } else {
+            for (int64_t g = threadIdx.x; g < G; g += kThreads) {
+                float f[16];
+                load_group<T, FULL>(row, k, g, f);
+                sq(f);
+            }
+        }
+        r_norm = norm_factor(block_sum_dd(hi, lo, red_d), k);
+    }
     float amax = 0.0f;
     if (resident) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const int64_t g = threadIdx.x + r * kThreads;
             if (g < G) {
-                load_group<T, FULL>(row, k, g, v[r]);
+                if constexpr (NORM == 0) load_group<T, FULL>(row, k, g, v[r]);
+                else normalize_group<NORM == 2>(v[r], r_norm, gain, k, g);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[r][j]));
             }
@@ -78,7 +200,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     } else {
         for (int64_t g = threadIdx.x; g < G; g += kThreads) {
             float f[16];
-            load_group<T, FULL>(row, k, g, f);
+            load(g, f);
 #pragma unroll
             for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(f[j]));
         }
@@ -103,7 +225,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     } else {
         for (int64_t g = threadIdx.x; g < G; g += kThreads) {
             float f[16];
-            load_group<T, FULL>(row, k, g, f);
+            load(g, f);
             emit(g, f);
         }
     }
@@ -116,35 +238,52 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     if (threadIdx.x == 0) s[t] = st;
 }
 
-template <typename T, bool FULL>
+template <typename T, bool FULL, int NORM>
 static void launch_rg(const T *x, int64_t m, int64_t k, int64_t kp, int8_t *q_nat, int8_t *q_perm, float *s,
-                      int32_t *sumq, hipStream_t st)
+                      int32_t *sumq, const float *gain, hipStream_t st)
 {
     const dim3 grid((unsigned)m), block(kThreads);
     const int64_t groups = ceil_div(k, 16);
     const int64_t rg = ceil_div(groups, kThreads);
     if (rg <= 1)
-        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 1>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s, sumq);
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 1, NORM>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s,
+                           sumq, gain);
     else if (rg == 2)
-        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 2>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s, sumq);
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, 2, NORM>), grid, block, 0, st, x, k, kp, q_nat, q_perm, s,
+                           sumq, gain);
     else
-        hipLaunchKernelGGL((act_quant_kernel<T, FULL, kResidentGroups>), grid, block, 0, st, x, k, kp, q_nat,
-                           q_perm, s, sumq);
+        hipLaunchKernelGGL((act_quant_kernel<T, FULL, kResidentGroups, NORM>), grid, block, 0, st, x, k, kp, q_nat,
+                           q_perm, s, sumq, gain);
+}
+
+template <int NORM>
+static void launch_any(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, int8_t *q_nat,
+                       int8_t *q_perm, float *s, int32_t *sumq, const float *gain, hipStream_t st)
+{
+    const bool full = k % 16 == 0;
+    if (bf16) {
+        const bf16_t *xb = static_cast<const bf16_t *>(x);
+        if (full) launch_rg<bf16_t, true, NORM>(xb, m, k, kp, q_nat, q_perm, s, sumq, gain, st);
+        else launch_rg<bf16_t, false, NORM>(xb, m, k, kp, q_nat, q_perm, s, sumq, gain, st);
+    } else {
+        const float *xf = static_cast<const float *>(x);
+        if (full) launch_rg<float, true, NORM>(xf, m, k, kp, q_nat, q_perm, s, sumq, gain, st);
+        else launch_rg<float, false, NORM>(xf, m, k, kp, q_nat, q_perm, s, sumq, gain, st);
+    }
 }
 
 hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, int8_t *q_nat,
                             int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
 {
-    const bool full = k % 16 == 0;
-    if (bf16) {
-        const bf16_t *xb = static_cast<const bf16_t *>(x);
-        if (full) launch_rg<bf16_t, true>(xb, m, k, kp, q_nat, q_perm, s, sumq, st);
-        else launch_rg<bf16_t, false>(xb, m, k, kp, q_nat, q_perm, s, sumq, st);
-    } else {
-        const float *xf = static_cast<const float *>(x);
-        if (full) launch_rg<float, true>(xf, m, k, kp, q_nat, q_perm, s, sumq, st);
-        else launch_rg<float, false>(xf, m, k, kp, q_nat, q_perm, s, sumq, st);
-    }
+    launch_any<0>(x, bf16, m, k, kp, q_nat, q_perm, s, sumq, nullptr, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_norm(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, const float *gain,
+                                 int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
+{
+    if (gain) launch_any<2>(x, bf16, m, k, kp, q_nat, q_perm, s, sumq, gain, st);
+    else launch_any<1>(x, bf16, m, k, kp, q_nat, q_perm, s, sumq, nullptr, st);
     return hipGetLastError();
 }
 

@@ -324,9 +324,15 @@ int bgemv_mode(int64_t m, int64_t k, bool bf16)
     // that every workgroup may quantize them all
     if (m <= 16 && k % 16 == 0 && k >= 1024 && m * k <= 32768 && bgemv_slots(m * k / 16) <= (bf16 ? 8 : 4))
         return 1;
+    return bgemv_prequant_supported(m, k) ? 2 : 0;
+}
+
+bool bgemv_prequant_supported(int64_t m, int64_t k)
+{
+    if (m < 5 || m > kBMaxTokens || k > kBMaxK) return false;
     const int64_t kp = round_up(k, 64);
     const int mb = bgemv_mb(m, kp);
-    return bgemv_slots(16 * mb * kp / 16) <= 16 && bgemv_lds(kp, mb) <= kBLdsMax ? 2 : 0;
+    return bgemv_slots(16 * mb * kp / 16) <= 16 && bgemv_lds(kp, mb) <= kBLdsMax;
 }
 
 namespace {

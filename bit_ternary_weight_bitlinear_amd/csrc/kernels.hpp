@@ -27,6 +27,10 @@ hipError_t launch_pad_weights(const uint8_t *src, int64_t n, int64_t k, int64_t 
 hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp,
                             int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st);
 
+// the same after a per-token RMS normalization x^ = (x * r) * gain (gain optional, [k])
+hipError_t launch_act_quant_norm(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, const float *gain,
+                                 int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st);
+
 // int8 [m][k] natural -> qperm [m][kp] + sumq[m]
 hipError_t launch_perm_q(const int8_t *q, int64_t m, int64_t k, int64_t kp, int8_t *q_perm,
                          int32_t *sumq, hipStream_t st);
@@ -53,6 +57,8 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
 // [m][kp] of the quantization kernel and pre_s / pre_sumq its scales and
 // sums; 0: neither (too many inputs for registers or LDS).
 int bgemv_mode(int64_t m, int64_t k, bool bf16);
+// whether the 5..64-token kernel takes these m, k with quantized rows (mode 2)
+bool bgemv_prequant_supported(int64_t m, int64_t k);
 hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st);
 
 // ---- MFMA GEMM on qperm activations

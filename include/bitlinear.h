@@ -59,7 +59,8 @@ typedef enum {
     BL_OP_FFN = 1,
     BL_OP_PACK = 2,
     BL_OP_GEMM_I32 = 3,
-    BL_OP_PACK_THRESHOLD = 4
+    BL_OP_PACK_THRESHOLD = 4,
+    BL_OP_FORWARD_NORM = 5
 } bl_op;
 
 /* Largest supported dimension (k, n, hidden, ffn) and token count m. */
@@ -73,6 +74,7 @@ typedef enum {
  *   BL_OP_PACK:      (m ignored, k, n)
  *   BL_OP_GEMM_I32:  (m, k, n)
  *   BL_OP_PACK_THRESHOLD: (m ignored, k, n)
+ *   BL_OP_FORWARD_NORM:   (m, k, n)
  * Returns 0 for invalid shapes and unknown ops as well; the operation itself
  * then reports the shape error.
  */
@@ -136,6 +138,37 @@ bl_status bitlinear_pack_weights_threshold(const float *w, int64_t n, int64_t k,
  */
 bl_status bitlinear_quant_act(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                               int8_t *q, float *scale, void *stream);
+
+/*
+ * Per-token RMS normalization fused into the absmax quantization: the
+ * normalization BitLinear applies to its input before quantizing it ("subln",
+ * "穿越1比特的奇幻旅程", section 架构创新: added for the stability of 1-bit
+ * training; "BitNet 中使用直通估计器工程化三元权重训练", section
+ * 工程化训练流程与参数配置: layer normalization keeping the variance, epsilon 1e-5).
+ * The pages give no formula; the form used is RMSNorm without mean subtraction
+ * or bias:
+ *   S = sum_k x^2 (fp64, each square exact; the sum equals the correctly rounded
+ *   fp64 sum except within ~k^2 2^-106 of a rounding boundary),
+ *   r = 1 / sqrt(fp32(S / k) + 1e-5) in fp32, x^ = (x * r) * gain[k] in fp32,
+ *   then q, scale as bitlinear_quant_act computes them for x^.
+ *   gain     optional fp32 [k], 16-byte aligned; NULL = no gain (all ones)
+ *   q, scale as in bitlinear_quant_act (scale = max(max_k |x^|, 1e-5))
+ */
+bl_status bitlinear_quant_act_norm(const void *x, bl_dtype dtype, int64_t m, int64_t k,
+                                   const float *gain, int8_t *q, float *scale, void *stream);
+
+/*
+ * BitLinear forward of RMS-normalized activations: bitlinear_forward applied to
+ * x^ of bitlinear_quant_act_norm, with the normalization fused into the
+ * quantization kernel (no x^ in memory).
+ *   gain       optional fp32 [k] (NULL = none)
+ *   workspace  >= bitlinear_workspace_size(BL_OP_FORWARD_NORM, m, k, n) bytes
+ * Other arguments and results as bitlinear_forward.
+ */
+bl_status bitlinear_forward_norm(const void *x, bl_dtype dtype, int64_t m, int64_t k, const float *gain,
+                                 const uint8_t *packed, const float *gamma, int64_t n,
+                                 float *y, int32_t *acc_out,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * BitLinear forward: y = (x quantized per token) x (ternary W)^T, rescaled

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, BL_ERR_VALUE = range(8)
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD = range(5)
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM = range(6)
 A = 0x10000          # aligned fake device address (never dereferenced)
 MIS = 0x10004        # 4-byte aligned only
 
@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward", "bitlinear_ffn",
               "bitlinear_gemm_i32", "bitlinear_workspace_size", "bitlinear_status_string",
-              "bitlinear_pack_weights_threshold"):
+              "bitlinear_pack_weights_threshold", "bitlinear_quant_act_norm", "bitlinear_forward_norm"):
         assert n in names
 
 
@@ -71,9 +71,11 @@ def test_op_numbering_matches_header():
     body = re.search(r"typedef enum \{([^}]*)\} bl_op;", text).group(1)
     vals = {k: int(v) for k, v in re.findall(r"(BL_OP_\w+)\s*=\s*(\d+)", body)}
     assert vals == {"BL_OP_FORWARD": OP_FORWARD, "BL_OP_FFN": OP_FFN, "BL_OP_PACK": OP_PACK,
-                    "BL_OP_GEMM_I32": OP_GEMM_I32, "BL_OP_PACK_THRESHOLD": OP_PACK_THRESHOLD}
+                    "BL_OP_GEMM_I32": OP_GEMM_I32, "BL_OP_PACK_THRESHOLD": OP_PACK_THRESHOLD,
+                    "BL_OP_FORWARD_NORM": OP_FORWARD_NORM}
     import bit_ternary_weight_bitlinear_amd as bl
-    assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32, bl.OP_PACK_THRESHOLD) == (0, 1, 2, 3, 4)
+    assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32, bl.OP_PACK_THRESHOLD,
+            bl.OP_FORWARD_NORM) == (0, 1, 2, 3, 4, 5)
 
 
 def test_forward_argument_errors(lib):
@@ -127,6 +129,21 @@ def test_other_entry_points_argument_errors(lib):
     assert ffn(A, 1, 1, 256, 510, A, A, A, A, A, A, A, None, None, A, 1 << 20, None) == BL_ERR_SHAPE
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, A, A, A, MIS, None, A, 1 << 20, None) == BL_ERR_ALIGN
     assert ffn(A, 1, 1, 256, 512, A, A, A, A, A, A, A, None, None, A, 16, None) == BL_ERR_WORKSPACE
+
+
+def test_norm_entry_points_argument_errors(lib):
+    qn = lib.bitlinear_quant_act_norm
+    assert qn(None, 1, 1, 256, None, A, A, None) == BL_ERR_NULL
+    assert qn(A, 3, 1, 256, None, A, A, None) == BL_ERR_DTYPE
+    assert qn(A, 1, 1, 254, None, A, A, None) == BL_ERR_SHAPE
+    assert qn(A, 1, 1, 256, MIS, A, A, None) == BL_ERR_ALIGN      # gain must be 16-byte aligned
+    fn = lib.bitlinear_forward_norm
+    need = lib.bitlinear_workspace_size(OP_FORWARD_NORM, 1, 256, 8)
+    assert need >= 256 * 256                                       # the quantized rows always go through it
+    assert fn(A, 1, 1, 256, None, A, A, 8, None, None, A, need, None) == BL_ERR_NULL
+    assert fn(A, 1, 1, 256, MIS, A, A, 8, A, None, A, need, None) == BL_ERR_ALIGN
+    assert fn(A, 1, 1, 256, None, A, A, 8, A, None, A, need - 1, None) == BL_ERR_WORKSPACE
+    assert fn(A, 1, 1, 256, None, A, A, 8, A, None, None, 0, None) == BL_ERR_NULL
 
 
 def test_noalloc_argument_errors(lib):

@@ -340,3 +340,38 @@ def test_forward_threshold_weights(bl, m, k, n):
     r = oracle.forward(x, p_ref, a_ref, k, "bf16")
     np.testing.assert_array_equal(host(acc), r["acc"])
     assert_y_close(host(y), r["y"])
+
+
+# ------------------------------------------------------------------ RMS norm before the quantization
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k,gain", [(1, 4, False), (3, 260, True), (4, 2560, True), (7, 6912, False),
+                                      (64, 4096, True), (2, 16388, True), (1027, 8196, False), (2, 20000, True)])
+def test_quant_act_norm_bit_exact(bl, dtype, m, k, gain):
+    x = synth.activations(140, m, k, dtype=dtype, outlier_channels=min(3, k), outlier_scale=30.0)
+    g = (1.0 + 0.25 * synth.normal(141, k)).astype(np.float32) if gain else None
+    q, s = bl.quant_act_norm(to_dev(x, dtype), to_dev(g) if gain else None)
+    q_ref, s_ref = oracle.quant_act_norm(x, dtype, g)
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+def test_quant_act_norm_hand_worked(bl, golden):
+    for c in golden["norm_cases"]:
+        g = to_dev(np.array(c["gain"], np.float32)) if "gain" in c else None
+        q, s = bl.quant_act_norm(to_dev(np.array(c["x_f32"], np.float32)), g)
+        np.testing.assert_array_equal(host(q), c["q"])
+        np.testing.assert_array_equal(host(s), np.array(c["s"], np.float32))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (1, 6912, 2560), (3, 260, 70), (8, 2560, 700),
+                                   (40, 6912, 300), (50, 14336, 64), (300, 2560, 256), (2048, 2560, 6912)])
+def test_forward_norm(bl, m, k, n):
+    w, p_ref, g_ref, _ = make_linear(142, 1, n, k)
+    x = synth.activations(142, m, k, dtype="bf16", outlier_channels=3, outlier_scale=20.0)
+    gain = (1.0 + 0.25 * synth.normal(143, k)).astype(np.float32)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward_norm(to_dev(x, "bf16"), packed, gamma, to_dev(gain), return_acc=True)
+    r = oracle.forward_norm(x, p_ref, g_ref, k, "bf16", gain)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
