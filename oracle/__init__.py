@@ -60,6 +60,7 @@ def _load():
     lib.oracle_threshold_ternarize.restype = ctypes.c_float
     lib.oracle_threshold_ternarize.argtypes = [_p, _i64, _i64, ctypes.c_float, _p, _p]
     lib.oracle_pack.argtypes = [_p, _i64, _i64, _p]
+    lib.oracle_pack_kmajor.argtypes = [_p, _i64, _i64, _p]
     lib.oracle_unpack.restype = _i64
     lib.oracle_unpack.argtypes = [_p, _i64, _i64, _p]
     lib.oracle_quant_act.argtypes = [_p, _i64, _i64, _p, _p]
@@ -132,6 +133,17 @@ def unpack(packed: np.ndarray, k: int) -> np.ndarray:
     bad = _load().oracle_unpack(_ptr(packed), n, k, _ptr(out))
     if bad:
         raise ValueError(f"{bad} invalid 2-bit codes (3) in packed weights")
+    return out
+
+
+def pack_kmajor(packed: np.ndarray, k: int) -> np.ndarray:
+    """Packed [n][k/4] -> the input-major packing [k][n/4] of the same codes (n % 4 == 0)."""
+    packed = _c(packed, np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] * 4 != k or n % 4:
+        raise ValueError("need packed [n][k/4] with n % 4 == 0")
+    out = np.empty((k, n // 4), dtype=np.uint8)
+    _load().oracle_pack_kmajor(_ptr(packed), n, k, _ptr(out))
     return out
 
 

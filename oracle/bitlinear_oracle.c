@@ -148,6 +148,24 @@ void oracle_pack(const int8_t *wt, int64_t n, int64_t k, uint8_t *packed)
         }
 }
 
+/* The same weights in the input-major ("K-major") order: the packing of the
+ * transposed ternary matrix. Row c of the output (one input feature) holds the
+ * codes of outputs r = 4j + i in bits 2i..2i+1 of byte j. Needs n % 4 == 0. */
+void oracle_pack_kmajor(const uint8_t *packed, int64_t n, int64_t k, uint8_t *out)
+{
+    const int64_t kb = k / 4, nb = n / 4;
+    for (int64_t c = 0; c < k; ++c)
+        for (int64_t j = 0; j < nb; ++j) {
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = 4 * j + i;
+                const unsigned code_r = (packed[r * kb + c / 4] >> (2 * (c % 4))) & 3u;
+                byte |= code_r << (2 * i);
+            }
+            out[c * nb + j] = (uint8_t)byte;
+        }
+}
+
 /* Inverse of oracle_pack. Returns the number of invalid codes (3) found; those
  * positions are written as 0. */
 int64_t oracle_unpack(const uint8_t *packed, int64_t n, int64_t k, int8_t *wt)

@@ -26,6 +26,7 @@ MUTANTS = [
     ("if (r < -1.0f) r = -1.0f;", ""),                                     # one-sided clip
     ("(int32_t)wt[r * k + c]", "(int32_t)wt[c * n + r]"),                  # transposed weights
     ("if (a > amax) amax = a;", "if (row[c] > amax) amax = row[c];"),      # max x, not max|x|
+    ("(packed[r * kb + c / 4] >> (2 * (c % 4)))", "(packed[r * kb + c / 4] >> (6 - 2 * (c % 4)))"),  # K-major field order
     # threshold quantizer
     ("if (a > delta) {", "if (a >= delta) {"),                              # >= instead of strict >
     ("const float delta = factor * mean;", "const float delta = mean;"),    # factor dropped

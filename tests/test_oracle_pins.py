@@ -169,6 +169,18 @@ def test_pack_roundtrip_and_no_code_three():
     np.testing.assert_array_equal(oracle.unpack(packed, 260), wt)
 
 
+def test_pack_kmajor_hand_worked_and_round_trip(golden):
+    c = golden["ffn_case"]
+    pd = np.array(c["packed_down"], np.uint8)
+    np.testing.assert_array_equal(oracle.pack_kmajor(pd, c["ffn"]), np.array(c["packed_down_kmajor"], np.uint8))
+    w = synth.weights(404, "W", 36, 52)
+    p, _, wt = oracle.pack_weights(w)
+    pt = oracle.pack_kmajor(p, 52)
+    assert pt.shape == (52, 9)
+    np.testing.assert_array_equal(oracle.unpack(pt, 36), wt.T)
+    np.testing.assert_array_equal(oracle.pack_kmajor(pt, 36), p)   # transposing twice is the identity
+
+
 def test_unpack_rejects_code_three():
     with pytest.raises(ValueError):
         oracle.unpack(np.array([[0x55, 0xC0]], np.uint8), 8)
