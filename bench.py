@@ -29,7 +29,7 @@ ceiling): once with the GEMV's grid and access pattern, once with the best
 grid found. `cpu_baseline` times the CPU oracle on bounded samples of every
 workload.
 
-`--profile decode|prefill|layer8|layer64|ffn1|ffn2048` runs one workload
+`--profile decode|prefill|layer8|layer64|ffn1|ffn1sparse|ffn2048` runs one workload
 eagerly (no graphs, no JSON line) for profilers: --steps steps, then one plain
 256 MiB device copy whose HBM byte counters calibrate those of the kernels.
 """
@@ -345,6 +345,29 @@ def bench_prefill(bl, torch, dev, tm, steps, warmup):
                 per_layer_tops=[round(o / v / 1e12, 1) for o, v in zip(ops, per)])
 
 
+def bench_ffn_sparse(bl, torch, tm, pool, x, steps, warmup, packed_bytes):
+    """The one-token FFN with the down projection reading only the rows of the
+    non-zero channels of h (input-major down weights, one copy per pool entry)."""
+    hid = x.shape[1]
+    f = pool[0][0][0].shape[0]
+    tpool = [(g, u, (bl.pack_kmajor(d[0]), d[1])) for g, u, d in pool]
+    ws = torch.empty(bl.workspace_size(bl.OP_FFN_SPARSE, 1, hid, f), dtype=torch.uint8, device=x.device)
+
+    def step(i):
+        g, u, dt = tpool[i % len(tpool)]
+        bl.ffn_sparse(x, g, u, dt, workspace=ws)
+
+    for i in range(warmup):
+        step(len(tpool) - 1 - (i % len(tpool)))
+    t = tm.steps_region(step, steps, len(tpool))
+    _, hq, _ = bl.ffn_sparse(x, *tpool[0], return_hq=True)
+    nz = float((hq != 0).float().mean().item())
+    read = (2 * f * hid + nz * f * hid) / 4   # gate and up, then the down rows of the non-zero channels
+    return dict(us_per_ffn=round(t * 1e6, 3), zero_channel_frac=round(1.0 - nz, 4),
+                weight_bytes_read=int(read), read_gbs=round(read / t / 1e9, 2),
+                packed_equiv_gbs=round(packed_bytes / t / 1e9, 2))
+
+
 def bench_ffn(bl, torch, dev, tm, steps, warmup, pool_mb):
     cfg = synth.WORKLOADS[5]
     hid, f = cfg["hidden"], cfg["ffn"]
@@ -371,6 +394,7 @@ def bench_ffn(bl, torch, dev, tm, steps, warmup, pool_mb):
         if m == 1:
             out["m1"] = dict(us_per_ffn=round(t * 1e6, 3), packed_gbs=round(packed_bytes / t / 1e9, 2),
                              frac_of_hbm_peak=r4(packed_bytes / t / 1e9 / HBM_PEAK_GBS), pool_bytes=pool_bytes)
+            out["m1_sparse_down"] = bench_ffn_sparse(bl, torch, tm, pool, x, steps, warmup, packed_bytes)
         else:
             out[f"m{m}"] = dict(ms_per_ffn=round(t * 1e3, 4), tops=round(ops / t / 1e12, 2),
                                 frac_of_int8_mfma_peak=r4(ops / t / 1e12 / INT8_MFMA_PEAK_TOPS))
@@ -412,17 +436,24 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
             ws = pool[i % len(pool)]
             for j in range(len(mats)):
                 bl.forward(xs[j], ws[j][0], ws[j][1], out=ys[j], workspace=wss[j] if wss[j].numel() > 1 else None)
-    elif what == "ffn1":
+    elif what in ("ffn1", "ffn1sparse"):
         cfg = synth.WORKLOADS[5]
         hid, f = cfg["hidden"], cfg["ffn"]
         mats = [make_weights(bl, torch, 5, "gate", f, hid, dev), make_weights(bl, torch, 5, "up", f, hid, dev),
                 make_weights(bl, torch, 5, "down", hid, f, dev)]
         pool, _ = rotation_pool(mats, pool_mb << 20)
         x = act_tensor(torch, 5, 1, hid, dev)
-        ws = torch.empty(bl.workspace_size(bl.OP_FFN, 1, hid, f), dtype=torch.uint8, device=dev)
-        for i in range(steps):
-            g, u, d = pool[i % len(pool)]
-            bl.ffn(x, g, u, d, workspace=ws)
+        if what == "ffn1":
+            ws = torch.empty(bl.workspace_size(bl.OP_FFN, 1, hid, f), dtype=torch.uint8, device=dev)
+            for i in range(steps):
+                g, u, d = pool[i % len(pool)]
+                bl.ffn(x, g, u, d, workspace=ws)
+        else:
+            tpool = [(g, u, (bl.pack_kmajor(d[0]), d[1])) for g, u, d in pool]
+            ws = torch.empty(bl.workspace_size(bl.OP_FFN_SPARSE, 1, hid, f), dtype=torch.uint8, device=dev)
+            for i in range(steps):
+                g, u, dt = tpool[i % len(tpool)]
+                bl.ffn_sparse(x, g, u, dt, workspace=ws)
     elif what == "ffn2048":
         cfg = synth.WORKLOADS[5]
         hid, f, m = cfg["hidden"], cfg["ffn"], max(cfg["ms"])
@@ -561,7 +592,7 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn2048"],
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn1sparse", "ffn2048"],
                     default=None, help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 

@@ -13,6 +13,8 @@ Functions mirror the C entry points:
   forward_norm(x, packed, gamma, gain=None) -> y fp32 [m][n] of the RMS-normalized x
   forward(x, packed, gamma)            -> y fp32 [m][n]        (return_acc=True adds acc)
   ffn(x, gate, up, down)               -> y fp32 [m][hidden]   (return_hq=True adds qh, sh)
+  pack_kmajor(packed)                  -> input-major copy [k][n/4] of packed [n][k/4]
+  ffn_sparse(x, gate, up, down_t)      -> ffn() for m <= 4 with an input-major down matrix
   gemm_i32(q, packed)                  -> acc int32 [m][n]
   workspace_size(op, m, k, n)          -> bytes
 Activations may be float32 or bfloat16 CUDA (HIP) tensors, contiguous, [m][k].
@@ -26,12 +28,12 @@ import torch
 
 __all__ = ["pack_weights", "pack_weights_threshold", "quant_act", "quant_act_norm", "forward_norm", "forward", "ffn", "gemm_i32", "workspace_size",
            "library_path", "load_library", "BitLinearError", "OP_FORWARD", "OP_FFN", "OP_PACK",
-           "OP_GEMM_I32", "OP_PACK_THRESHOLD", "OP_FORWARD_NORM"]
+           "OP_GEMM_I32", "OP_PACK_THRESHOLD", "OP_FORWARD_NORM", "OP_FFN_SPARSE", "pack_kmajor", "ffn_sparse"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM = 0, 1, 2, 3, 4, 5  # bl_op
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE = range(7)  # bl_op
 _F32, _BF16 = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -53,6 +55,9 @@ _SIGNATURES = {
                                    _c_p, _c_size, _c_p]),
     "bitlinear_ffn": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                _c_p, _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
+    "bitlinear_pack_kmajor": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
+    "bitlinear_ffn_sparse": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
     "bitlinear_gemm_i32": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
 }
 
@@ -275,6 +280,44 @@ def ffn(x: torch.Tensor, gate, up, down, *, return_hq: bool = False,
                              y.data_ptr(), hq.data_ptr() if hq is not None else None,
                              hs.data_ptr() if hs is not None else None, wp, wn, _stream(x.device)),
            "bitlinear_ffn")
+    return (y, hq, hs) if return_hq else y
+
+
+def pack_kmajor(packed: torch.Tensor):
+    """packed [n][k/4] -> the input-major packing [k][n/4] of the same codes (n % 4 == 0)."""
+    lib = load_library()
+    n, kb = packed.shape
+    out = torch.empty((4 * kb, n // 4), dtype=torch.uint8, device=packed.device)
+    _check(lib.bitlinear_pack_kmajor(_dev(packed, "packed", torch.uint8), n, 4 * kb, out.data_ptr(),
+                                     _stream(packed.device)), "bitlinear_pack_kmajor")
+    return out
+
+
+def ffn_sparse(x: torch.Tensor, gate, up, down_t, *, return_hq: bool = False,
+               workspace: torch.Tensor | None = None):
+    """Decode FFN (m <= 4) skipping the zero channels of h in the down projection.
+    gate/up are (packed [ffn][hidden/4], gamma); down_t is (pack_kmajor(down packed), gamma)."""
+    lib = load_library()
+    m, hidden = x.shape
+    ffn_dim = gate[0].shape[0]
+    if gate[0].shape[1] * 4 != hidden or up[0].shape != gate[0].shape or \
+            down_t[0].shape != (ffn_dim, hidden // 4):
+        raise BitLinearError("FFN weight shapes do not match")
+    y = torch.empty((m, hidden), dtype=torch.float32, device=x.device)
+    hq = torch.empty((m, ffn_dim), dtype=torch.int8, device=x.device) if return_hq else None
+    hs = torch.empty(m, dtype=torch.float32, device=x.device) if return_hq else None
+    ws = (_caller_workspace(workspace, OP_FFN_SPARSE, m, hidden, ffn_dim) if workspace is not None
+          else _workspace(OP_FFN_SPARSE, m, hidden, ffn_dim, x.device))
+    wp, wn = _ws_args(ws)
+    _check(lib.bitlinear_ffn_sparse(_dev(x, "x"), _act_dtype(x), m, hidden, ffn_dim,
+                                    _dev(gate[0], "gate_packed", torch.uint8),
+                                    _dev(gate[1], "gate_gamma", torch.float32),
+                                    _dev(up[0], "up_packed", torch.uint8), _dev(up[1], "up_gamma", torch.float32),
+                                    _dev(down_t[0], "down_packed_t", torch.uint8),
+                                    _dev(down_t[1], "down_gamma", torch.float32),
+                                    y.data_ptr(), hq.data_ptr() if hq is not None else None,
+                                    hs.data_ptr() if hs is not None else None, wp, wn, _stream(x.device)),
+           "bitlinear_ffn_sparse")
     return (y, hq, hs) if return_hq else y
 
 

@@ -106,6 +106,39 @@ FfnLayout ffn_layout(void *ws, int64_t m, int64_t hidden, int64_t ffn)
     return L;
 }
 
+struct SparseFfnLayout {
+    int64_t hp;
+    int64_t parts;
+    float *h = nullptr, *hmax = nullptr, *s = nullptr;
+    int32_t *partial = nullptr;  // [slices of ffn][m][hidden]
+    uint8_t *gpad = nullptr, *upad = nullptr;
+    int64_t bytes = 0;
+};
+
+SparseFfnLayout sparse_ffn_layout(void *ws, int64_t m, int64_t hidden, int64_t ffn)
+{
+    SparseFfnLayout L;
+    L.hp = round_up(hidden, 64);
+    L.parts = gemv_grid(ffn, L.hp, true);
+    Carve c(ws);
+    L.h = c.take<float>(m * ffn * 4);
+    L.hmax = c.take<float>(L.parts * m * 4);
+    L.s = c.take<float>(m * 4);
+    L.partial = c.take<int32_t>(sparse_down_partials(hidden, ffn) * m * hidden * 4);
+    if (hidden % 64) {
+        L.gpad = c.take<uint8_t>(ffn * (L.hp / 4));
+        L.upad = c.take<uint8_t>(ffn * (L.hp / 4));
+    }
+    L.bytes = c.off;
+    return L;
+}
+
+bool sparse_ffn_shape_ok(int64_t m, int64_t hidden, int64_t ffn)
+{
+    return m >= 1 && m <= 4 && kdim_ok(hidden) && hidden % 16 == 0 && kdim_ok(ffn) &&
+           gemv_supported(m, round_up(hidden, 64));
+}
+
 bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
 // argument checks of the forward (shared by bitlinear_forward and its variant
@@ -186,6 +219,9 @@ size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n)
     case BL_OP_FORWARD_NORM:
         if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return 0;
         return (size_t)forward_layout(nullptr, m, k, n, true).bytes;
+    case BL_OP_FFN_SPARSE:
+        if (!sparse_ffn_shape_ok(m, k, n)) return 0;
+        return (size_t)sparse_ffn_layout(nullptr, m, k, n).bytes;
     default:
         return 0;
     }
@@ -344,6 +380,53 @@ bl_status bitlinear_forward_noalloc(const void *x, bl_dtype dtype, int64_t m, in
     }
     return bitlinear_forward(x, dtype, m, k, packed, gamma, n, y, acc_out, ws,
                              need > 0 ? (size_t)BL_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
+bl_status bitlinear_pack_kmajor(const uint8_t *packed, int64_t n, int64_t k, uint8_t *packed_t, void *stream)
+{
+    if (!packed || !packed_t) return BL_ERR_NULL;
+    if (!dim_ok(n) || n % 4 || !kdim_ok(k)) return BL_ERR_SHAPE;
+    if (!aligned16(packed) || !aligned16(packed_t)) return BL_ERR_ALIGN;
+    return hip_status(launch_pack_kmajor(packed, n, k, packed_t, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_ffn_sparse(const void *x, bl_dtype dtype, int64_t m, int64_t hidden, int64_t ffn,
+                               const uint8_t *gate_packed, const float *gate_gamma, const uint8_t *up_packed,
+                               const float *up_gamma, const uint8_t *down_packed_t, const float *down_gamma,
+                               float *y, int8_t *hq_out, float *hs_out, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    if (!x || !gate_packed || !gate_gamma || !up_packed || !up_gamma || !down_packed_t || !down_gamma || !y)
+        return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!sparse_ffn_shape_ok(m, hidden, ffn)) return BL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(gate_packed) || !aligned16(up_packed) || !aligned16(down_packed_t) ||
+        !aligned16(y) || !aligned(gate_gamma, 4) || !aligned(up_gamma, 4) || !aligned(down_gamma, 4) ||
+        (hq_out && !aligned16(hq_out)) || (hs_out && !aligned(hs_out, 4)))
+        return BL_ERR_ALIGN;
+    const SparseFfnLayout need = sparse_ffn_layout(nullptr, m, hidden, ffn);
+    if (const bl_status w = check_ws(workspace, workspace_bytes, need.bytes)) return w;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const SparseFfnLayout L = sparse_ffn_layout(workspace, m, hidden, ffn);
+    const uint8_t *wg = gate_packed, *wu = up_packed;
+    if (L.gpad) {
+        if (hipError_t e = launch_pad_weights(gate_packed, ffn, hidden, L.hp, L.gpad, st)) return hip_status(e);
+        if (hipError_t e = launch_pad_weights(up_packed, ffn, hidden, L.hp, L.upad, st)) return hip_status(e);
+        wg = L.gpad;
+        wu = L.upad;
+    }
+    GemvProblem p{};
+    p.x = x; p.bf16 = dtype == BL_BF16; p.m = m; p.k = hidden; p.kp = L.hp; p.n = ffn;
+    p.w0 = wg; p.w1 = wu; p.ldw = L.hp / 4; p.gamma0 = gate_gamma; p.gamma1 = up_gamma;
+    p.out = L.h; p.hmax_part = L.hmax;
+    if (hipError_t e = launch_gemv(p, st)) return hip_status(e);
+    SparseDownProblem d{};
+    d.h = L.h; d.hmax_part = L.hmax; d.parts = L.parts; d.m = m; d.ffn = ffn; d.hidden = hidden;
+    d.wt = down_packed_t; d.gamma = down_gamma; d.y = y;
+    d.partial = L.partial; d.s = L.s;
+    d.q_out = hq_out; d.s_out = hs_out;
+    return hip_status(launch_sparse_down(d, st));
 }
 
 bl_status bitlinear_gemm_i32(const int8_t *q, int64_t m, int64_t k, const uint8_t *packed, int64_t n,

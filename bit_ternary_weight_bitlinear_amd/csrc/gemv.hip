@@ -47,6 +47,7 @@ struct GemvArgs {
     int32_t *acc_out;
     int8_t *q_out;
     float *s_out;
+    float *hmax_part;   // gate/up pair only, optional: max |h| per (workgroup, token)
     int rows_per_wg;  // R
     int chunks;       // kp / 64
 };
@@ -324,20 +325,44 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     __syncthreads();
 
     // 5. rescale: y = (float)acc * ((s / 127) * gamma); the pair gives h = relu(g)^2 * u
+    float hmax[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const float ca = token_scale(st[t], a.gamma0[0]);
         const float cb = DUAL ? token_scale(st[t], a.gamma1[0]) : 0.0f;
+        hmax[t] = 0.0f;
         for (int r = tid; r < rows; r += kGT) {
             const int va = acc_lds[t * R + r] - sq[t];
             const float ya = (float)va * ca;
             float *o = a.out + t * a.n + r0 + r;
             if constexpr (DUAL) {
                 const int vb = acc_lds[(MT + t) * R + r] - sq[t];
-                *o = sq_relu_gate(ya, (float)vb * cb);
+                const float h = sq_relu_gate(ya, (float)vb * cb);
+                *o = h;
+                hmax[t] = fmaxf(hmax[t], fabsf(h));
             } else {
                 *o = ya;
                 if (a.acc_out) a.acc_out[t * a.n + r0 + r] = va;
+            }
+        }
+    }
+    if constexpr (DUAL) {
+        // the requantization's absmax, one partial per workgroup and token
+        if (a.hmax_part) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const float mw = wave_max(hmax[t]);
+                if (lane == 0) red_f[t][wave] = mw;
+            }
+            __syncthreads();
+            if (tid < MT) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    if (t == tid)
+#pragma unroll
+                        for (int w = 0; w < kGW; ++w) mx = fmaxf(mx, red_f[t][w]);
+                a.hmax_part[(int64_t)blockIdx.x * MT + tid] = mx;
             }
         }
     }
@@ -456,6 +481,11 @@ void dispatch(const GemvProblem &p, int jm, dim3 grid, size_t lds, hipStream_t s
 
 }  // namespace
 
+int64_t gemv_grid(int64_t n, int64_t kp, bool dual)
+{
+    return ceil_div(n, gemv_rows_per_wg(n, kp / 64, dual));
+}
+
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
 {
     GemvArgs a;
@@ -463,6 +493,7 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw;
     a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out; a.q_out = p.q_out; a.s_out = p.s_out;
+    a.hmax_part = p.hmax_part;
     a.chunks = (int)(p.kp / 64);
     const bool dual = p.w1 != nullptr;
     const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);

@@ -49,8 +49,11 @@ struct GemvProblem {
     float *s_out;            // optional per-token scales
     const float *pre_s;      // 5..64-token kernel, mode 2 only (see bgemv_mode)
     const int32_t *pre_sumq;
+    float *hmax_part;        // gate/up pair, optional: max |h| per (workgroup, token), [grid][m]
 };
 bool gemv_supported(int64_t m, int64_t kp);
+// workgroups of a decode launch (the number of hmax_part rows it writes)
+int64_t gemv_grid(int64_t n, int64_t kp, bool dual);
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
 // 5..64 tokens, single matrix, k <= 8192. Mode 1 (up to 16 tokens):
 // quantization inside the launch; mode 2: x holds the qperm int8 rows
@@ -60,6 +63,27 @@ int bgemv_mode(int64_t m, int64_t k, bool bf16);
 // whether the 5..64-token kernel takes these m, k with quantized rows (mode 2)
 bool bgemv_prequant_supported(int64_t m, int64_t k);
 hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st);
+
+// ---- decode FFN down projection over the input-major weights, skipping the
+// zero channels of the requantized h (sparse_down.hip)
+// packed [n][k/4] -> input-major [k][n/4] (n % 4 == 0)
+hipError_t launch_pack_kmajor(const uint8_t *packed, int64_t n, int64_t k, uint8_t *packed_t, hipStream_t st);
+struct SparseDownProblem {
+    const float *h;          // [m][ffn] fp32 (the gate/up launch's output)
+    const float *hmax_part;  // [parts][m] partial maxima of |h|
+    int64_t parts;
+    int64_t m, ffn, hidden;
+    const uint8_t *wt;       // input-major down weights [ffn][hidden/4]
+    const float *gamma;
+    float *y;                // [m][hidden]
+    int32_t *partial;        // [sparse_down_partials()][m][hidden] int32 scratch
+    float *s;                // [m] fp32 scratch (the row scales of h)
+    int8_t *q_out;           // optional [m][ffn]
+    float *s_out;            // optional [m]
+};
+int64_t sparse_down_nslices(int64_t hidden);
+int64_t sparse_down_partials(int64_t hidden, int64_t ffn);
+hipError_t launch_sparse_down(const SparseDownProblem &p, hipStream_t st);
 
 // ---- MFMA GEMM on qperm activations
 enum GemmEpilogue { EPI_Y = 0, EPI_ACC = 1, EPI_GATE = 2 };

@@ -60,7 +60,8 @@ typedef enum {
     BL_OP_PACK = 2,
     BL_OP_GEMM_I32 = 3,
     BL_OP_PACK_THRESHOLD = 4,
-    BL_OP_FORWARD_NORM = 5
+    BL_OP_FORWARD_NORM = 5,
+    BL_OP_FFN_SPARSE = 6
 } bl_op;
 
 /* Largest supported dimension (k, n, hidden, ffn) and token count m. */
@@ -75,6 +76,7 @@ typedef enum {
  *   BL_OP_GEMM_I32:  (m, k, n)
  *   BL_OP_PACK_THRESHOLD: (m ignored, k, n)
  *   BL_OP_FORWARD_NORM:   (m, k, n)
+ *   BL_OP_FFN_SPARSE:     (m, hidden, ffn)
  * Returns 0 for invalid shapes and unknown ops as well; the operation itself
  * then reports the shape error.
  */
@@ -229,6 +231,35 @@ bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden
 bl_status bitlinear_forward_noalloc(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                                     const uint8_t *packed, const float *gamma, int64_t n,
                                     float *y, int32_t *acc_out, void *stream);
+
+/*
+ * Input-major copy of packed weights (offline, once per weight): the codes of
+ * packed [n][k/4] rearranged as packed_t [k][n/4], row c holding the codes of
+ * outputs 4j+i of input c in bits 2i..2i+1 of byte j -- the packing of the
+ * transposed ternary matrix. Used for the FFN's down projection by
+ * bitlinear_ffn_sparse. Requires n % 4 == 0 and k % 4 == 0.
+ */
+bl_status bitlinear_pack_kmajor(const uint8_t *packed, int64_t n, int64_t k, uint8_t *packed_t, void *stream);
+
+/*
+ * bitlinear_ffn for decode (1 <= m <= 4 tokens) with the down projection reading
+ * only the weights of the non-zero channels of the requantized h
+ * ("BitNet 1-bit LLM 的混合精度微调技术", operational-parameter paragraph: with the
+ * squared-ReLU GLU gating, only the non-zero channels are computed). The down
+ * weights come input-major (bitlinear_pack_kmajor of the [hidden][ffn/4]
+ * matrix), so a channel whose code is 0 for every token skips its whole row.
+ * Results are those of bitlinear_ffn: zero codes contribute nothing.
+ *   down_packed_t  uint8 [ffn][hidden/4] (input-major)
+ *   workspace      >= bitlinear_workspace_size(BL_OP_FFN_SPARSE, m, hidden, ffn)
+ * Other arguments as bitlinear_ffn. Requires m <= 4, hidden % 16 == 0 and
+ * ffn % 4 == 0 (BL_ERR_SHAPE otherwise).
+ */
+bl_status bitlinear_ffn_sparse(const void *x, bl_dtype dtype, int64_t m, int64_t hidden, int64_t ffn,
+                               const uint8_t *gate_packed, const float *gate_gamma,
+                               const uint8_t *up_packed, const float *up_gamma,
+                               const uint8_t *down_packed_t, const float *down_gamma,
+                               float *y, int8_t *hq_out, float *hs_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The bare ternary x int8 contraction ("穿越1比特的奇幻旅程", section

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, BL_ERR_VALUE = range(8)
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM = range(6)
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE = range(7)
 A = 0x10000          # aligned fake device address (never dereferenced)
 MIS = 0x10004        # 4-byte aligned only
 
@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward", "bitlinear_ffn",
               "bitlinear_gemm_i32", "bitlinear_workspace_size", "bitlinear_status_string",
-              "bitlinear_pack_weights_threshold", "bitlinear_quant_act_norm", "bitlinear_forward_norm"):
+              "bitlinear_pack_weights_threshold", "bitlinear_quant_act_norm", "bitlinear_forward_norm",
+              "bitlinear_pack_kmajor", "bitlinear_ffn_sparse"):
         assert n in names
 
 
@@ -72,10 +73,10 @@ def test_op_numbering_matches_header():
     vals = {k: int(v) for k, v in re.findall(r"(BL_OP_\w+)\s*=\s*(\d+)", body)}
     assert vals == {"BL_OP_FORWARD": OP_FORWARD, "BL_OP_FFN": OP_FFN, "BL_OP_PACK": OP_PACK,
                     "BL_OP_GEMM_I32": OP_GEMM_I32, "BL_OP_PACK_THRESHOLD": OP_PACK_THRESHOLD,
-                    "BL_OP_FORWARD_NORM": OP_FORWARD_NORM}
+                    "BL_OP_FORWARD_NORM": OP_FORWARD_NORM, "BL_OP_FFN_SPARSE": OP_FFN_SPARSE}
     import bit_ternary_weight_bitlinear_amd as bl
     assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32, bl.OP_PACK_THRESHOLD,
-            bl.OP_FORWARD_NORM) == (0, 1, 2, 3, 4, 5)
+            bl.OP_FORWARD_NORM, bl.OP_FFN_SPARSE) == (0, 1, 2, 3, 4, 5, 6)
 
 
 def test_forward_argument_errors(lib):
@@ -144,6 +145,24 @@ def test_norm_entry_points_argument_errors(lib):
     assert fn(A, 1, 1, 256, MIS, A, A, 8, A, None, A, need, None) == BL_ERR_ALIGN
     assert fn(A, 1, 1, 256, None, A, A, 8, A, None, A, need - 1, None) == BL_ERR_WORKSPACE
     assert fn(A, 1, 1, 256, None, A, A, 8, A, None, None, 0, None) == BL_ERR_NULL
+
+
+def test_sparse_ffn_argument_errors(lib):
+    pk = lib.bitlinear_pack_kmajor
+    assert pk(None, 8, 256, A, None) == BL_ERR_NULL
+    assert pk(A, 6, 256, A, None) == BL_ERR_SHAPE                 # n % 4 != 0
+    assert pk(A, 8, 256, MIS, None) == BL_ERR_ALIGN
+    f = lib.bitlinear_ffn_sparse
+    ws = lib.bitlinear_workspace_size
+    need = ws(OP_FFN_SPARSE, 1, 4096, 14336)
+    assert need >= 14336 * 4 + 4096 * 4                             # h and the down sums
+    assert ws(OP_FFN_SPARSE, 5, 4096, 14336) == 0                   # decode only
+    assert ws(OP_FFN_SPARSE, 1, 4104, 14336) == 0                   # hidden % 16 != 0
+    assert f(A, 1, 1, 4096, 14336, A, A, A, A, None, A, A, None, None, A, need, None) == BL_ERR_NULL
+    assert f(A, 1, 5, 4096, 14336, A, A, A, A, A, A, A, None, None, A, need, None) == BL_ERR_SHAPE
+    assert f(A, 1, 1, 4104, 14336, A, A, A, A, A, A, A, None, None, A, need, None) == BL_ERR_SHAPE
+    assert f(A, 1, 1, 4096, 14336, A, A, A, A, MIS, A, A, None, None, A, need, None) == BL_ERR_ALIGN
+    assert f(A, 1, 1, 4096, 14336, A, A, A, A, A, A, A, None, None, A, need - 1, None) == BL_ERR_WORKSPACE
 
 
 def test_noalloc_argument_errors(lib):

@@ -375,3 +375,74 @@ def test_forward_norm(bl, m, k, n):
     r = oracle.forward_norm(x, p_ref, g_ref, k, "bf16", gain)
     np.testing.assert_array_equal(host(acc), r["acc"])
     assert_y_close(host(y), r["y"])
+
+
+# ------------------------------------------------------------------ decode FFN skipping zero channels of h
+
+@pytest.mark.parametrize("n,k", [(4, 4), (8, 260), (300, 512), (4096, 14336)])
+def test_pack_kmajor_bit_exact(bl, n, k):
+    w, p_ref, _, _ = make_linear(150, 1, n, k)
+    pt = bl.pack_kmajor(to_dev(p_ref))
+    np.testing.assert_array_equal(host(pt), oracle.pack_kmajor(p_ref, k))
+
+
+def _ffn_sparse_case(bl, cfg, m, hid, f, dtype="bf16", x=None):
+    x = synth.activations(cfg, m, hid, dtype=dtype) if x is None else x
+    dev_w, ref_w = {}, {}
+    for name, shape in (("gate", (f, hid)), ("up", (f, hid)), ("down", (hid, f))):
+        w, p_ref, g_ref, _ = make_linear(cfg, name, *shape)
+        dev_w[name] = bl.pack_weights(to_dev(w))
+        ref_w[name] = (p_ref, g_ref)
+    down_t = (bl.pack_kmajor(dev_w["down"][0]), dev_w["down"][1])
+    y, hq, hs = bl.ffn_sparse(to_dev(x, dtype), dev_w["gate"], dev_w["up"], down_t, return_hq=True)
+    r = oracle.ffn(x, ref_w["gate"], ref_w["up"], ref_w["down"], hid, f, dtype)
+    np.testing.assert_array_equal(host(hq), r["qh"])
+    np.testing.assert_array_equal(host(hs).view(np.uint32), r["sh"].view(np.uint32))
+    assert_y_close(host(y), r["y"])
+    # the dense FFN gives the same bits
+    y_dense = bl.ffn(to_dev(x, dtype), dev_w["gate"], dev_w["up"], dev_w["down"])
+    np.testing.assert_array_equal(host(y).view(np.uint32), host(y_dense).view(np.uint32))
+    return r
+
+
+@pytest.mark.parametrize("m,hid,f", [(1, 256, 512), (2, 256, 1000), (3, 272, 516), (4, 512, 1024),
+                                     (1, 1024, 20000), (1, 4096, 14336), (4, 4096, 14336)])
+def test_ffn_sparse(bl, m, hid, f):
+    _ffn_sparse_case(bl, 160, m, hid, f)
+
+
+def test_ffn_sparse_repeated_calls(bl):
+    """Calls in a row on one workspace, different inputs: every call writes all
+    of the scratch it reads, so each matches the oracle."""
+    hid, f = 512, 2048
+    ws = torch.empty(bl.workspace_size(bl.OP_FFN_SPARSE, 2, hid, f), dtype=torch.uint8, device="cuda")
+    mats = {name: make_linear(161, name, *shape) for name, shape in
+            (("gate", (f, hid)), ("up", (f, hid)), ("down", (hid, f)))}
+    dev = {k: bl.pack_weights(to_dev(v[0])) for k, v in mats.items()}
+    down_t = (bl.pack_kmajor(dev["down"][0]), dev["down"][1])
+    for rep in range(4):
+        x = synth.activations(170 + rep, 2, hid, dtype="bf16")
+        y = bl.ffn_sparse(to_dev(x, "bf16"), dev["gate"], dev["up"], down_t, workspace=ws)
+        r = oracle.ffn(x, mats["gate"][1:3], mats["up"][1:3], mats["down"][1:3], hid, f, "bf16")
+        assert_y_close(host(y), r["y"])
+
+
+def test_ffn_sparse_all_zero_and_dense_h(bl):
+    """Degenerate sparsity: every channel of h zero (x = 0), and no channel zero
+    (h > 0 everywhere: gate and up weights all positive, x > 0)."""
+    hid, f = 256, 512
+    x0 = np.zeros((1, hid), np.float32)
+    _ffn_sparse_case(bl, 162, 1, hid, f, dtype="f32", x=x0)
+    dev_w, ref_w = {}, {}
+    pos = np.full((f, hid), 0.01, np.float32)
+    for name, w in (("gate", pos), ("up", pos), ("down", synth.weights(163, "down", hid, f))):
+        p_ref, g_ref, _ = oracle.pack_weights(w)
+        dev_w[name] = bl.pack_weights(to_dev(w))
+        ref_w[name] = (p_ref, g_ref)
+    x = np.abs(synth.activations(163, 1, hid, dtype="f32")) + np.float32(0.5)
+    down_t = (bl.pack_kmajor(dev_w["down"][0]), dev_w["down"][1])
+    y, hq, hs = bl.ffn_sparse(to_dev(x), dev_w["gate"], dev_w["up"], down_t, return_hq=True)
+    r = oracle.ffn(x, ref_w["gate"], ref_w["up"], ref_w["down"], hid, f, "f32")
+    assert np.all(r["qh"] != 0)
+    np.testing.assert_array_equal(host(hq), r["qh"])
+    assert_y_close(host(y), r["y"])
