@@ -17,6 +17,10 @@ the order the pages give:
   rms norm (subln) before the activation quantization, per token:
             S = sum_k x^2 (correctly rounded fp64)  ->  ms = fp32(S / k)
             ->  r = 1 / sqrt(ms + 1e-5) (fp32)  ->  x^ = (x * r) * g  ->  absmax int8 of x^
+  4-bit activations (W1.58A4), per token: keep |x| >= the keep-th largest
+            |x| (top-K, ties kept)  ->  s = max(max|x|, 1e-5)  ->  v = x * (6 / s)
+            ->  nearest E2M1 value e (ties to even), stored doubled (2e in [-12, 12])
+            ->  the same int32 product  ->  y = acc * (s / 12) * gamma
   threshold pack (a second weight quantizer): delta = factor * mean|W|
             ->  W~ = sign(W) where |W| > delta, else 0  ->  alpha = mean(|W| * mask)
             ->  the same 2-bit codes; alpha takes gamma's place in forward/ffn
@@ -67,6 +71,10 @@ def _load():
     lib.oracle_bf16_to_f32.argtypes = [_p, _i64, _p]
     lib.oracle_matmul_i32.argtypes = [_p, _i64, _i64, _p, _i64, _p]
     lib.oracle_rescale.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, _p]
+    lib.oracle_rescale_q.argtypes = [_p, _i64, _i64, _p, ctypes.c_float, ctypes.c_float, _p]
+    lib.oracle_e2m1_doubled.restype = ctypes.c_int
+    lib.oracle_e2m1_doubled.argtypes = [ctypes.c_float]
+    lib.oracle_quant_act_a4.argtypes = [_p, _i64, _i64, _i64, _p, _p]
     lib.oracle_sqrelu_gate.argtypes = [_p, _p, _i64, _p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -237,6 +245,33 @@ def matmul_i32(q: np.ndarray, wt: np.ndarray) -> np.ndarray:
     return acc
 
 
+def e2m1_doubled(v: float) -> int:
+    """Nearest E2M1 value of a float32, doubled (an integer in [-12, 12])."""
+    return int(_load().oracle_e2m1_doubled(float(np.float32(v))))
+
+
+def quant_act_a4(x: np.ndarray, dtype: str = "f32", keep: int | None = None):
+    """4-bit activations: (q int8 [m][k] holding 2e, s fp32 [m]); keep defaults to ceil(k / 2)."""
+    xf = _as_f32_acts(x, dtype)
+    m, k = xf.shape
+    keep = (k + 1) // 2 if keep is None else int(keep)
+    if not 1 <= keep <= k:
+        raise ValueError("keep must be in [1, k]")
+    q = np.empty((m, k), dtype=np.int8)
+    s = np.empty(m, dtype=np.float32)
+    _load().oracle_quant_act_a4(_ptr(xf), m, k, keep, _ptr(q), _ptr(s))
+    return q, s
+
+
+def rescale_q(acc: np.ndarray, s: np.ndarray, gamma, qmax: float) -> np.ndarray:
+    acc = _c(acc, np.int32)
+    s = _c(s, np.float32)
+    m, n = acc.shape
+    y = np.empty((m, n), dtype=np.float32)
+    _load().oracle_rescale_q(_ptr(acc), m, n, _ptr(s), float(np.float32(gamma)), float(np.float32(qmax)), _ptr(y))
+    return y
+
+
 def rescale(acc: np.ndarray, s: np.ndarray, gamma) -> np.ndarray:
     acc = _c(acc, np.int32)
     s = _c(s, np.float32)
@@ -272,6 +307,14 @@ def forward_norm(x: np.ndarray, packed: np.ndarray, gamma, k: int, dtype: str = 
     r = forward(xn, packed, gamma, k, "f32")
     r["xn"] = xn
     return r
+
+
+def forward_a4(x: np.ndarray, packed: np.ndarray, gamma, k: int, dtype: str = "f32", keep: int | None = None):
+    """W1.58A4 forward: 4-bit top-K activations, the int32 product, y = acc * (s / 12) * gamma."""
+    wt = unpack(packed, k)
+    q, s = quant_act_a4(x, dtype, keep)
+    acc = matmul_i32(q, wt)
+    return dict(q=q, s=s, acc=acc, y=rescale_q(acc, s, gamma, 12.0))
 
 
 def ffn(x: np.ndarray, gate, up, down, hidden: int, ffn_dim: int, dtype: str = "bf16"):

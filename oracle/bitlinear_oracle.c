@@ -16,6 +16,9 @@
  *  [P4] "BitNet 三元权重阈值优化工程实践" (blog.hotdry.top, 2025-09-08), section
  *       on the core principle of ternary threshold optimization (the threshold
  *       quantizer and its code).
+ *  [P1'] [P1], the paragraph on progressive quantization (second stage: 4-bit
+ *       activations in the MinMax FP4 format with E2M1 bits, top-K
+ *       sparsification of 50 % for outlier channels).
  *
  * Every function is a direct loop over the definition. Floating point follows
  * the precision the kernels decide integers in (fp32), with the operation order
@@ -34,6 +37,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -206,6 +210,55 @@ void oracle_quant_act(const float *x, int64_t m, int64_t k, int8_t *q, float *s)
     }
 }
 
+/* Nearest E2M1 value of v (the FP4 grid 0, 0.5, 1, 1.5, 2, 3, 4, 6 and its
+ * negatives), returned doubled as an integer in [-12, 12]. Ties go to the value
+ * whose mantissa bit is 0 (0, 1, 2, 4): round half to even on that grid. */
+int oracle_e2m1_doubled(float v)
+{
+    const float a = fabsf(v);
+    int c;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 6;
+    else if (a <= 5.0f) c = 8;
+    else c = 12;
+    return v < 0.0f ? -c : c;
+}
+
+static int desc_float(const void *pa, const void *pb)
+{
+    const float a = *(const float *)pa, b = *(const float *)pb;
+    return (a < b) - (a > b);
+}
+
+/* 4-bit activations [P1']: per token, the entries whose magnitude is at least
+ * the keep-th largest magnitude are kept (top-K; entries tied with that value
+ * are all kept), the rest become 0; the kept entries are scaled so that the
+ * largest magnitude s = max(max|x|, 1e-5) maps to 6, the largest E2M1 value
+ * (MinMax), v = x * (6 / s) with one fp32 division per token, and rounded to
+ * the nearest E2M1 value. q holds the doubled value 2e (an integer in
+ * [-12, 12], so q * s / 12 approximates x); s is stored per token. */
+void oracle_quant_act_a4(const float *x, int64_t m, int64_t k, int64_t keep, int8_t *q, float *s)
+{
+    float *mag = (float *)malloc((size_t)k * sizeof(float));
+    for (int64_t t = 0; t < m; ++t) {
+        const float *row = x + t * k;
+        for (int64_t c = 0; c < k; ++c) mag[c] = fabsf(row[c]);
+        qsort(mag, (size_t)k, sizeof(float), desc_float);
+        const float tau = mag[keep - 1];
+        const float amax = mag[0];
+        const float st = amax > ORACLE_EPS ? amax : ORACLE_EPS;
+        const float inv = 6.0f / st;
+        for (int64_t c = 0; c < k; ++c)
+            q[t * k + c] = fabsf(row[c]) >= tau ? (int8_t)oracle_e2m1_doubled(row[c] * inv) : 0;
+        s[t] = st;
+    }
+    free(mag);
+}
+
 /* acc[t][r] = sum_c q[t][c] * wt[r][c], exact in int32 (the W1.58A8 product,
  * [P3 推理实现 / GPU端]). */
 void oracle_matmul_i32(const int8_t *q, int64_t m, int64_t k,
@@ -219,6 +272,18 @@ void oracle_matmul_i32(const int8_t *q, int64_t m, int64_t k,
                 sum += (int32_t)q[t * k + c] * (int32_t)wt[r * k + c];
             acc[t * n + r] = sum;
         }
+}
+
+/* y = acc * gamma * s / qmax: undo both quantization scales (qmax = 127 for
+ * the int8 codes, 12 for the doubled E2M1 codes). */
+void oracle_rescale_q(const int32_t *acc, int64_t m, int64_t n,
+                      const float *s, float gamma, float qmax, float *y)
+{
+    for (int64_t t = 0; t < m; ++t) {
+        const float ct = (s[t] / qmax) * gamma;
+        for (int64_t r = 0; r < n; ++r)
+            y[t * n + r] = (float)acc[t * n + r] * ct;
+    }
 }
 
 /* y = acc * gamma * s / 127: undo both quantization scales. */

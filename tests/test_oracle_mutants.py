@@ -27,6 +27,11 @@ MUTANTS = [
     ("(int32_t)wt[r * k + c]", "(int32_t)wt[c * n + r]"),                  # transposed weights
     ("if (a > amax) amax = a;", "if (row[c] > amax) amax = row[c];"),      # max x, not max|x|
     ("(packed[r * kb + c / 4] >> (2 * (c % 4)))", "(packed[r * kb + c / 4] >> (6 - 2 * (c % 4)))"),  # K-major field order
+    # 4-bit activations
+    ("fabsf(row[c]) >= tau ?", "fabsf(row[c]) > tau ?"),                    # ties at the top-K threshold dropped
+    ("if (a <= 0.25f) c = 0;", "if (a < 0.25f) c = 0;"),                   # E2M1 tie away from even
+    ("const float inv = 6.0f / st;", "const float inv = 7.0f / st;"),      # wrong FP4 range
+    ("const float tau = mag[keep - 1];", "const float tau = mag[keep > 1 ? keep - 2 : 0];"),  # off-by-one top-K
     # threshold quantizer
     ("if (a > delta) {", "if (a >= delta) {"),                              # >= instead of strict >
     ("const float delta = factor * mean;", "const float delta = mean;"),    # factor dropped
@@ -48,6 +53,7 @@ PY_MUTANTS = [
     ("d = np.float32(ms + NORM_EPS)", "d = np.float32(ms)"),                           # epsilon dropped
     ("r = np.float32(np.float32(1.0) / np.sqrt(d))", "r = np.float32(np.float32(1.0) / d)"),  # no square root
     ("            row = row * g", "            row = row"),                           # gain dropped
+    ("rescale_q(acc, s, gamma, 12.0)", "rescale_q(acc, s, gamma, 6.0)"),                  # A4 step not doubled
 ]
 
 
