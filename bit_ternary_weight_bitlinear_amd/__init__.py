@@ -11,6 +11,8 @@ Functions mirror the C entry points:
   quant_act(x)                         -> (q int8 [m][k], scale fp32 [m])
   quant_act_norm(x, gain=None)         -> the same for the RMS-normalized x
   forward_norm(x, packed, gamma, gain=None) -> y fp32 [m][n] of the RMS-normalized x
+  quant_act_a4(x, keep=None)           -> (q int8 [m][k] doubled E2M1 codes, scale fp32 [m])
+  forward_a4(x, packed, gamma, keep=None) -> y fp32 [m][n] of the W1.58A4 product
   forward(x, packed, gamma)            -> y fp32 [m][n]        (return_acc=True adds acc)
   ffn(x, gate, up, down)               -> y fp32 [m][hidden]   (return_hq=True adds qh, sh)
   pack_kmajor(packed)                  -> input-major copy [k][n/4] of packed [n][k/4]
@@ -28,12 +30,14 @@ import torch
 
 __all__ = ["pack_weights", "pack_weights_threshold", "quant_act", "quant_act_norm", "forward_norm", "forward", "ffn", "gemm_i32", "workspace_size",
            "library_path", "load_library", "BitLinearError", "OP_FORWARD", "OP_FFN", "OP_PACK",
-           "OP_GEMM_I32", "OP_PACK_THRESHOLD", "OP_FORWARD_NORM", "OP_FFN_SPARSE", "pack_kmajor", "ffn_sparse"]
+           "OP_GEMM_I32", "OP_PACK_THRESHOLD", "OP_FORWARD_NORM", "OP_FFN_SPARSE", "OP_FORWARD_A4",
+           "pack_kmajor", "ffn_sparse", "quant_act_a4", "forward_a4"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE = range(7)  # bl_op
+(OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE,
+ OP_FORWARD_A4) = range(8)  # bl_op in include/bitlinear.h
 _F32, _BF16 = 0, 1
 
 _c_i64 = ctypes.c_int64
@@ -55,6 +59,9 @@ _SIGNATURES = {
                                    _c_p, _c_size, _c_p]),
     "bitlinear_ffn": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                _c_p, _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
+    "bitlinear_quant_act_a4": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "bitlinear_forward_a4": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                      _c_p, _c_size, _c_p]),
     "bitlinear_pack_kmajor": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "bitlinear_ffn_sparse": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
@@ -230,6 +237,42 @@ def forward_norm(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, gai
                                       _dev(packed, "packed", torch.uint8), _dev(gamma, "gamma", torch.float32), n,
                                       _dev(y, "y", torch.float32), acc.data_ptr() if acc is not None else None,
                                       wp, wn, _stream(x.device)), "bitlinear_forward_norm")
+    return (y, acc) if return_acc else y
+
+
+def quant_act_a4(x: torch.Tensor, keep: int | None = None):
+    """4-bit activations [m][k] -> (q int8 [m][k] holding 2e, scale fp32 [m]); keep defaults to ceil(k / 2)."""
+    lib = load_library()
+    m, k = x.shape
+    keep = (k + 1) // 2 if keep is None else int(keep)
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    s = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(lib.bitlinear_quant_act_a4(_dev(x, "x"), _act_dtype(x), m, k, keep, q.data_ptr(), s.data_ptr(),
+                                      _stream(x.device)), "bitlinear_quant_act_a4")
+    return q, s
+
+
+def forward_a4(x: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, keep: int | None = None,
+               *, return_acc: bool = False, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None):
+    """W1.58A4 forward: 4-bit top-K activations times the ternary weights."""
+    lib = load_library()
+    m, k = x.shape
+    n = packed.shape[0]
+    keep = (k + 1) // 2 if keep is None else int(keep)
+    if packed.shape[1] * 4 != k:
+        raise BitLinearError("packed weights do not match the activation width")
+    if out is not None:
+        _check_out(out, (m, n), torch.float32, "out")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=x.device) if return_acc else None
+    ws = (_caller_workspace(workspace, OP_FORWARD_A4, m, k, n) if workspace is not None
+          else _workspace(OP_FORWARD_A4, m, k, n, x.device))
+    wp, wn = _ws_args(ws)
+    _check(lib.bitlinear_forward_a4(_dev(x, "x"), _act_dtype(x), m, k, keep, _dev(packed, "packed", torch.uint8),
+                                    _dev(gamma, "gamma", torch.float32), n, _dev(y, "y", torch.float32),
+                                    acc.data_ptr() if acc is not None else None, wp, wn, _stream(x.device)),
+           "bitlinear_forward_a4")
     return (y, acc) if return_acc else y
 
 

@@ -23,6 +23,16 @@
 // so hi + lo rounds to the correctly rounded S unless S lies within about
 // k^2 2^-106 of a rounding boundary of fp64. The fp32 steps after it are
 // single correctly rounded operations (no contraction in this build).
+//
+// A4 (act_quant_a4_kernel): 4-bit activations ("BitNet 1-bit LLM 的混合精度微调
+// 技术", paragraph on progressive quantization: MinMax FP4 with E2M1 bits, top-K
+// sparsification of 50 %). Per token, the keep-th largest magnitude tau is
+// found by a radix select on the fp32 bits of |x| (non-negative floats order
+// like their bit patterns), two bits per pass from the top, each pass counting
+// the candidates per digit and reducing the counts over the workgroup (no
+// atomics); entries with |x| >= tau are kept, v = x * (6 / s) with s =
+// max(max|x|, 1e-5), and v goes to the nearest E2M1 value (ties to the even
+// mantissa), stored doubled as an int8 code in [-12, 12].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -132,6 +142,37 @@ __device__ inline void normalize_group(float f[16], float r, const float *gain, 
     }
 }
 
+// The nearest E2M1 value of v (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives),
+// doubled; at a midpoint the value with mantissa bit 0 (0, 1, 2, 4) wins.
+__device__ inline int e2m1_doubled(float v)
+{
+    const float a = fabsf(v);
+    const int c = a <= 0.25f ? 0 : a < 0.75f ? 1 : a <= 1.25f ? 2 : a < 1.75f ? 3 : a <= 2.5f ? 4 : a < 3.5f ? 6
+                : a <= 5.0f ? 8 : 12;
+    return v < 0.0f ? -c : c;
+}
+
+// three counts summed over the workgroup; red alternates between two halves
+// (parity) so one barrier per call suffices
+__device__ inline int3 block_sum3(int3 c, int (*red)[3][4], int parity)
+{
+    c.x = wave_sum(c.x);
+    c.y = wave_sum(c.y);
+    c.z = wave_sum(c.z);
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        red[parity][0][w] = c.x;
+        red[parity][1][w] = c.y;
+        red[parity][2][w] = c.z;
+    }
+    __syncthreads();
+    int3 r;
+    r.x = red[parity][0][0] + red[parity][0][1] + red[parity][0][2] + red[parity][0][3];
+    r.y = red[parity][1][0] + red[parity][1][1] + red[parity][1][2] + red[parity][1][3];
+    r.z = red[parity][2][0] + red[parity][2][1] + red[parity][2][2] + red[parity][2][3];
+    return r;
+}
+
 }  // namespace
 
 constexpr int kResidentGroups = 4;
@@ -238,6 +279,130 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
     if (threadIdx.x == 0) s[t] = st;
 }
 
+// 4-bit activations: one workgroup per token, 256 threads, as act_quant_kernel
+template <typename T, bool FULL, int RG>
+__global__ __launch_bounds__(256) void act_quant_a4_kernel(const T *__restrict__ x, int64_t k, int64_t kp,
+                                                           int64_t keep, int8_t *__restrict__ q_nat,
+                                                           int8_t *__restrict__ q_perm, float *__restrict__ s,
+                                                           int32_t *__restrict__ sumq)
+{
+    __shared__ float red_f[4];
+    __shared__ int red_i[4];
+    __shared__ int red3[2][3][4];
+    const int64_t t = blockIdx.x;
+    const T *row = x + t * k;
+    const int64_t G = ceil_div(k, 16);
+    const bool resident = G <= (int64_t)RG * kThreads;
+
+    float v[RG][16];
+    float amax = 0.0f;
+    if (resident) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int64_t g = threadIdx.x + r * kThreads;
+            if (g < G) {
+                load_group<T, FULL>(row, k, g, v[r]);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[r][j]));
+            }
+        }
+    } else {
+        for (int64_t g = threadIdx.x; g < G; g += kThreads) {
+            float f[16];
+            load_group<T, FULL>(row, k, g, f);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        }
+    }
+    amax = block_max(amax, red_f);
+
+    // radix select of tau, the keep-th largest |x|, two bits per pass. Inputs
+    // past k (the zero padding of the last group) are not candidates.
+    constexpr int LOW = sizeof(T) == 2 ? 16 : 0;  // bf16: the low 16 bits are zero
+    uint32_t prefix = 0, pmask = 0;
+    int want = (int)keep;
+    int parity = 0;
+    for (int b = 30; b >= LOW; b -= 2) {
+        int3 c = make_int3(0, 0, 0);  // candidates with digit >= 1, >= 2, == 3
+        auto count = [&](const float f[16], int64_t g) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t key = __float_as_uint(fabsf(f[j]));
+                if ((FULL || 16 * g + j < k) && (key & pmask) == prefix) {
+                    const uint32_t d = (key >> b) & 3u;
+                    c.x += d >= 1u;
+                    c.y += d >= 2u;
+                    c.z += d == 3u;
+                }
+            }
+        };
+        if (resident) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const int64_t g = threadIdx.x + r * kThreads;
+                if (g < G) count(v[r], g);
+            }
+        } else {
+            for (int64_t g = threadIdx.x; g < G; g += kThreads) {
+                float f[16];
+                load_group<T, FULL>(row, k, g, f);
+                count(f, g);
+            }
+        }
+        const int3 tot = block_sum3(c, red3, parity);
+        parity ^= 1;
+        uint32_t d;
+        if (tot.z >= want) d = 3u;
+        else if (tot.y >= want) { d = 2u; want -= tot.z; }
+        else if (tot.x >= want) { d = 1u; want -= tot.y; }
+        else { d = 0u; want -= tot.x; }
+        prefix |= d << b;
+        pmask |= 3u << b;
+    }
+    const uint32_t tau = prefix;  // the keep-th largest |x| (as bits)
+    const float st = fmaxf(amax, kEps);
+    const float inv = 6.0f / st;
+
+    int qsum = 0;
+    auto emit = [&](int64_t g, const float f[16]) {
+        int qi[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            qi[j] = __float_as_uint(fabsf(f[j])) >= tau ? e2m1_doubled(f[j] * inv) : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qsum += qi[j];
+        if (q_perm) *reinterpret_cast<uint4 *>(q_perm + t * kp + 16 * g) = qperm_pack(qi);
+        if (q_nat) {
+            uint32_t d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                d[i] = (uint32_t)(qi[4 * i] & 0xFF) | ((uint32_t)(qi[4 * i + 1] & 0xFF) << 8) |
+                       ((uint32_t)(qi[4 * i + 2] & 0xFF) << 16) | ((uint32_t)(qi[4 * i + 3] & 0xFF) << 24);
+            store_nat(q_nat + t * k, k, g, make_uint4(d[0], d[1], d[2], d[3]));
+        }
+    };
+    if (resident) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int64_t g = threadIdx.x + r * kThreads;
+            if (g < G) emit(g, v[r]);
+        }
+    } else {
+        for (int64_t g = threadIdx.x; g < G; g += kThreads) {
+            float f[16];
+            load_group<T, FULL>(row, k, g, f);
+            emit(g, f);
+        }
+    }
+    if (q_perm) {
+        for (int64_t g = G + threadIdx.x; g < kp / 16; g += kThreads)
+            *reinterpret_cast<uint4 *>(q_perm + t * kp + 16 * g) = make_uint4(0, 0, 0, 0);
+        const int total = block_sum(qsum, red_i);
+        if (threadIdx.x == 0) sumq[t] = total;
+    }
+    if (threadIdx.x == 0) s[t] = st;
+}
+
 template <typename T, bool FULL, int NORM>
 static void launch_rg(const T *x, int64_t m, int64_t k, int64_t kp, int8_t *q_nat, int8_t *q_perm, float *s,
                       int32_t *sumq, const float *gain, hipStream_t st)
@@ -276,6 +441,39 @@ hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int6
                             int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
 {
     launch_any<0>(x, bf16, m, k, kp, q_nat, q_perm, s, sumq, nullptr, st);
+    return hipGetLastError();
+}
+
+template <typename T, bool FULL>
+static void launch_a4_rg(const T *x, int64_t m, int64_t k, int64_t kp, int64_t keep, int8_t *q_nat, int8_t *q_perm,
+                         float *s, int32_t *sumq, hipStream_t st)
+{
+    const dim3 grid((unsigned)m), block(kThreads);
+    const int64_t rg = ceil_div(ceil_div(k, 16), kThreads);
+    if (rg <= 1)
+        hipLaunchKernelGGL((act_quant_a4_kernel<T, FULL, 1>), grid, block, 0, st, x, k, kp, keep, q_nat, q_perm, s,
+                           sumq);
+    else if (rg == 2)
+        hipLaunchKernelGGL((act_quant_a4_kernel<T, FULL, 2>), grid, block, 0, st, x, k, kp, keep, q_nat, q_perm, s,
+                           sumq);
+    else
+        hipLaunchKernelGGL((act_quant_a4_kernel<T, FULL, kResidentGroups>), grid, block, 0, st, x, k, kp, keep,
+                           q_nat, q_perm, s, sumq);
+}
+
+hipError_t launch_act_quant_a4(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, int64_t keep,
+                               int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st)
+{
+    const bool full = k % 16 == 0;
+    if (bf16) {
+        const bf16_t *xb = static_cast<const bf16_t *>(x);
+        if (full) launch_a4_rg<bf16_t, true>(xb, m, k, kp, keep, q_nat, q_perm, s, sumq, st);
+        else launch_a4_rg<bf16_t, false>(xb, m, k, kp, keep, q_nat, q_perm, s, sumq, st);
+    } else {
+        const float *xf = static_cast<const float *>(x);
+        if (full) launch_a4_rg<float, true>(xf, m, k, kp, keep, q_nat, q_perm, s, sumq, st);
+        else launch_a4_rg<float, false>(xf, m, k, kp, keep, q_nat, q_perm, s, sumq, st);
+    }
     return hipGetLastError();
 }
 

@@ -219,6 +219,9 @@ size_t bitlinear_workspace_size(int op, int64_t m, int64_t k, int64_t n)
     case BL_OP_FORWARD_NORM:
         if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return 0;
         return (size_t)forward_layout(nullptr, m, k, n, true).bytes;
+    case BL_OP_FORWARD_A4:
+        if (!tokens_ok(m) || !kdim_ok(k) || !dim_ok(n)) return 0;
+        return (size_t)forward_layout(nullptr, m, k, n, true).bytes;
     case BL_OP_FFN_SPARSE:
         if (!sparse_ffn_shape_ok(m, k, n)) return 0;
         return (size_t)sparse_ffn_layout(nullptr, m, k, n).bytes;
@@ -293,6 +296,25 @@ bl_status bitlinear_quant_act_norm(const void *x, bl_dtype dtype, int64_t m, int
                                             nullptr, static_cast<hipStream_t>(stream)));
 }
 
+// The contraction of activations quantized into the workspace (qperm rows,
+// scales, code sums) by one of the quantization kernels; qmax as in token_scale.
+bl_status prequant_contraction(const FwdLayout &L, int64_t m, int64_t k, int64_t n, const uint8_t *w,
+                               const float *gamma, float *y, int32_t *acc_out, float qmax, hipStream_t st)
+{
+    if (bgemv_prequant_supported(m, k)) {  // 5..64 tokens, k <= 8192
+        GemvProblem bp{};
+        bp.x = L.qp; bp.bf16 = false; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
+        bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma; bp.out = y; bp.acc_out = acc_out;
+        bp.pre_s = L.s; bp.pre_sumq = L.sumq; bp.qmax = qmax;
+        return hip_status(launch_bgemv(bp, st));
+    }
+    GemmProblem g{};
+    g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
+    g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
+    g.out = y; g.acc_out = acc_out; g.epi = EPI_Y; g.qmax = qmax;
+    return hip_status(launch_contraction(g, st));
+}
+
 bl_status bitlinear_forward_norm(const void *x, bl_dtype dtype, int64_t m, int64_t k, const float *gain,
                                  const uint8_t *packed, const float *gamma, int64_t n, float *y, int32_t *acc_out,
                                  void *workspace, size_t workspace_bytes, void *stream)
@@ -311,18 +333,40 @@ bl_status bitlinear_forward_norm(const void *x, bl_dtype dtype, int64_t m, int64
     }
     if (hipError_t e = launch_act_quant_norm(x, dtype == BL_BF16, m, k, L.kp, gain, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
-    if (bgemv_prequant_supported(m, k)) {  // 5..64 tokens, k <= 8192
-        GemvProblem bp{};
-        bp.x = L.qp; bp.bf16 = false; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
-        bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma; bp.out = y; bp.acc_out = acc_out;
-        bp.pre_s = L.s; bp.pre_sumq = L.sumq;
-        return hip_status(launch_bgemv(bp, st));
+    return prequant_contraction(L, m, k, n, w, gamma, y, acc_out, 127.0f, st);
+}
+
+bl_status bitlinear_quant_act_a4(const void *x, bl_dtype dtype, int64_t m, int64_t k, int64_t keep, int8_t *q,
+                                 float *scale, void *stream)
+{
+    if (!x || !q || !scale) return BL_ERR_NULL;
+    if (dtype != BL_F32 && dtype != BL_BF16) return BL_ERR_DTYPE;
+    if (!tokens_ok(m) || !kdim_ok(k)) return BL_ERR_SHAPE;
+    if (keep < 1 || keep > k) return BL_ERR_VALUE;
+    if (!aligned16(x) || !aligned16(q) || !aligned(scale, 4)) return BL_ERR_ALIGN;
+    return hip_status(launch_act_quant_a4(x, dtype == BL_BF16, m, k, round_up(k, 64), keep, q, nullptr, scale,
+                                          nullptr, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_forward_a4(const void *x, bl_dtype dtype, int64_t m, int64_t k, int64_t keep,
+                               const uint8_t *packed, const float *gamma, int64_t n, float *y, int32_t *acc_out,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (const bl_status a = forward_args(x, dtype, m, k, packed, gamma, n, y, acc_out)) return a;
+    if (keep < 1 || keep > k) return BL_ERR_VALUE;
+    const FwdLayout need = forward_layout(nullptr, m, k, n, true);
+    if (const bl_status w = check_ws(workspace, workspace_bytes, need.bytes)) return w;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdLayout L = forward_layout(workspace, m, k, n, true);
+    const uint8_t *w = packed;
+    if (L.wpad) {
+        if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
+        w = L.wpad;
     }
-    GemmProblem g{};
-    g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
-    g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
-    g.out = y; g.acc_out = acc_out; g.epi = EPI_Y;
-    return hip_status(launch_contraction(g, st));
+    if (hipError_t e = launch_act_quant_a4(x, dtype == BL_BF16, m, k, L.kp, keep, nullptr, L.qp, L.s, L.sumq, st))
+        return hip_status(e);
+    return prequant_contraction(L, m, k, n, w, gamma, y, acc_out, 12.0f, st);
 }
 
 bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k, const uint8_t *packed,

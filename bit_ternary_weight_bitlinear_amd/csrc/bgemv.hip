@@ -53,6 +53,7 @@ struct BgemvArgs {
     const float *gamma;
     float *out;
     int32_t *acc_out;
+    float qmax;
     int rows_per_wg;  // R
     int chunks;       // kp / 64
 };
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 #pragma unroll
             for (int w = eb; w < kBW; w += RB) va += part[((w * MB + mb) * 4 + v) * 64 + el];
             const int64_t o = (int64_t)(t0 + t) * a.n + r0 + row;
-            a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0]);
+            a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0], a.qmax);
             if (a.acc_out) a.acc_out[o] = va;
         }
     }
@@ -380,7 +381,7 @@ hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
     a.x = p.x; a.pre_s = p.pre_s; a.pre_sumq = p.pre_sumq;
     a.m = p.m; a.k = p.k; a.kp = p.kp; a.n = p.n;
     a.w = p.w0; a.ldw = p.ldw; a.gamma = p.gamma0;
-    a.out = p.out; a.acc_out = p.acc_out;
+    a.out = p.out; a.acc_out = p.acc_out; a.qmax = p.qmax;
     a.chunks = (int)(p.kp / 64);
     int64_t r = ceil_div(p.n, (int64_t)256);
     if (r > kBMaxRows) r = kBMaxRows;

@@ -252,8 +252,11 @@ __device__ inline uint4 qperm_pack(const int q[16])
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-// Rescale of one accumulator: y = (float)acc * ((s / 127) * gamma)
+// Rescale of one accumulator: y = (float)acc * ((s / 127) * gamma); qmax is the
+// code of the largest magnitude (127 for int8 activations, 12 for the doubled
+// E2M1 codes of 4-bit activations)
 __device__ inline float token_scale(float s, float gamma) { return (s / 127.0f) * gamma; }
+__device__ inline float token_scale(float s, float gamma, float qmax) { return (s / qmax) * gamma; }
 
 __device__ inline float sq_relu_gate(float g, float u)
 {

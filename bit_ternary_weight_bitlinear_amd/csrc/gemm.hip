@@ -54,6 +54,7 @@ struct GemmArgs {
     const float *gamma0, *gamma1;
     float *out;
     int32_t *acc_out;
+    float qmax;
     int n_tiles, m_tiles;
 };
 
@@ -164,8 +165,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
                     const float se[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        c0e[e] = token_scale(se[e], g0);
-                        if constexpr (DUAL) c1e[e] = token_scale(se[e], g1);
+                        c0e[e] = token_scale(se[e], g0, a.qmax);
+                        if constexpr (DUAL) c1e[e] = token_scale(se[e], g1, a.qmax);
                     }
                 }
 #pragma unroll
@@ -560,7 +561,7 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t st)
     GemmArgs a;
     a.qp = p.qp; a.kp = p.kp; a.s = p.s; a.sumq = p.sumq; a.m = p.m; a.n = p.n;
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw; a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
-    a.out = p.out; a.acc_out = p.acc_out;
+    a.out = p.out; a.acc_out = p.acc_out; a.qmax = p.qmax;
     a.n_tiles = a.m_tiles = 0;
     switch (p.epi) {
     case EPI_Y: return launch_epi<EPI_Y>(a, st);

@@ -31,6 +31,11 @@ hipError_t launch_act_quant(const void *x, bool bf16, int64_t m, int64_t k, int6
 hipError_t launch_act_quant_norm(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, const float *gain,
                                  int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st);
 
+// 4-bit activations: top-`keep` magnitudes per token kept, MinMax E2M1, codes stored
+// doubled (2e in [-12, 12]) in the same outputs as launch_act_quant
+hipError_t launch_act_quant_a4(const void *x, bool bf16, int64_t m, int64_t k, int64_t kp, int64_t keep,
+                               int8_t *q_nat, int8_t *q_perm, float *s, int32_t *sumq, hipStream_t st);
+
 // int8 [m][k] natural -> qperm [m][kp] + sumq[m]
 hipError_t launch_perm_q(const int8_t *q, int64_t m, int64_t k, int64_t kp, int8_t *q_perm,
                          int32_t *sumq, hipStream_t st);
@@ -49,6 +54,7 @@ struct GemvProblem {
     float *s_out;            // optional per-token scales
     const float *pre_s;      // 5..64-token kernel, mode 2 only (see bgemv_mode)
     const int32_t *pre_sumq;
+    float qmax = 127.0f;     // mode 2: code of the largest magnitude (127 int8, 12 doubled E2M1)
     float *hmax_part;        // gate/up pair, optional: max |h| per (workgroup, token), [grid][m]
 };
 bool gemv_supported(int64_t m, int64_t kp);
@@ -99,6 +105,7 @@ struct GemmProblem {
     float *out;        // EPI_Y: y; EPI_GATE: h
     int32_t *acc_out;  // EPI_Y: optional; EPI_ACC: required
     int epi;
+    float qmax = 127.0f;  // code of the largest magnitude: 127 (int8) or 12 (doubled E2M1)
 };
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t st);
 

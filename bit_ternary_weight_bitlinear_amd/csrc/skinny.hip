@@ -34,6 +34,7 @@ struct SkinnyArgs {
     const float *gamma0, *gamma1;
     float *out;
     int32_t *acc_out;
+    float qmax;
 };
 
 // MB: 16-token blocks (1..4). EPI as for the GEMM. KB > 0: each wave has at
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
         float c0 = 0.0f, c1 = 0.0f;
         if constexpr (EPI != EPI_ACC) {
             const float s = a.s[m];
-            c0 = token_scale(s, a.gamma0[0]);
-            if constexpr (DUAL) c1 = token_scale(s, a.gamma1[0]);
+            c0 = token_scale(s, a.gamma0[0], a.qmax);
+            if constexpr (DUAL) c1 = token_scale(s, a.gamma1[0], a.qmax);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -214,7 +215,7 @@ hipError_t launch_skinny(const GemmProblem &p, hipStream_t st)
     SkinnyArgs a;
     a.qp = p.qp; a.kp = p.kp; a.s = p.s; a.sumq = p.sumq; a.m = p.m; a.n = p.n;
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw; a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
-    a.out = p.out; a.acc_out = p.acc_out;
+    a.out = p.out; a.acc_out = p.acc_out; a.qmax = p.qmax;
     switch ((p.m + 15) / 16) {
     case 1: launch_mb1(a, p.epi, st); break;
     case 2: launch_mb<2>(a, p.epi, st); break;

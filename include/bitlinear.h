@@ -61,7 +61,8 @@ typedef enum {
     BL_OP_GEMM_I32 = 3,
     BL_OP_PACK_THRESHOLD = 4,
     BL_OP_FORWARD_NORM = 5,
-    BL_OP_FFN_SPARSE = 6
+    BL_OP_FFN_SPARSE = 6,
+    BL_OP_FORWARD_A4 = 7
 } bl_op;
 
 /* Largest supported dimension (k, n, hidden, ffn) and token count m. */
@@ -77,6 +78,7 @@ typedef enum {
  *   BL_OP_PACK_THRESHOLD: (m ignored, k, n)
  *   BL_OP_FORWARD_NORM:   (m, k, n)
  *   BL_OP_FFN_SPARSE:     (m, hidden, ffn)
+ *   BL_OP_FORWARD_A4:     (m, k, n)
  * Returns 0 for invalid shapes and unknown ops as well; the operation itself
  * then reports the shape error.
  */
@@ -231,6 +233,35 @@ bl_status bitlinear_ffn(const void *x, bl_dtype dtype, int64_t m, int64_t hidden
 bl_status bitlinear_forward_noalloc(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                                     const uint8_t *packed, const float *gamma, int64_t n,
                                     float *y, int32_t *acc_out, void *stream);
+
+/*
+ * 4-bit activations for the W1.58A4 variant ("BitNet 1-bit LLM 的混合精度微调技术",
+ * paragraph on progressive quantization: activations brought to 4 bits in the
+ * MinMax FP4 format with E2M1 bits, top-K sparsification of 50 % against
+ * outlier channels). The pages give no formula; the form used, per token:
+ *   tau  = the keep-th largest |x|; entries with |x| >= tau are kept (ties at
+ *          tau all kept), the others become 0
+ *   s    = max(max_k |x|, 1e-5); v = x * (6 / s) (one fp32 division per token)
+ *   e    = the nearest E2M1 value to v (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ *          negatives), ties to the value whose mantissa bit is 0
+ *   q    = 2e, an int8 in [-12, 12], so that x ~ q * s / 12
+ *   keep    1..k (BL_ERR_VALUE otherwise); the pages' 50 % is keep = ceil(k / 2)
+ *   q, scale  int8 [m][k] and fp32 [m] (output)
+ */
+bl_status bitlinear_quant_act_a4(const void *x, bl_dtype dtype, int64_t m, int64_t k, int64_t keep,
+                                 int8_t *q, float *scale, void *stream);
+
+/*
+ * W1.58A4 forward: the 4-bit codes of bitlinear_quant_act_a4 times the ternary
+ * weights, y = (float)acc * ((s / 12) * gamma), acc = sum_k q[m][k] * w~[n][k]
+ * (exact in int32: the doubled E2M1 codes are small integers).
+ *   workspace  >= bitlinear_workspace_size(BL_OP_FORWARD_A4, m, k, n) bytes
+ * Other arguments and results as bitlinear_forward.
+ */
+bl_status bitlinear_forward_a4(const void *x, bl_dtype dtype, int64_t m, int64_t k, int64_t keep,
+                               const uint8_t *packed, const float *gamma, int64_t n,
+                               float *y, int32_t *acc_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Input-major copy of packed weights (offline, once per weight): the codes of

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, BL_ERR_VALUE = range(8)
-OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE = range(7)
+OP_FORWARD, OP_FFN, OP_PACK, OP_GEMM_I32, OP_PACK_THRESHOLD, OP_FORWARD_NORM, OP_FFN_SPARSE, OP_FORWARD_A4 = range(8)
 A = 0x10000          # aligned fake device address (never dereferenced)
 MIS = 0x10004        # 4-byte aligned only
 
@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward", "bitlinear_ffn",
               "bitlinear_gemm_i32", "bitlinear_workspace_size", "bitlinear_status_string",
               "bitlinear_pack_weights_threshold", "bitlinear_quant_act_norm", "bitlinear_forward_norm",
-              "bitlinear_pack_kmajor", "bitlinear_ffn_sparse"):
+              "bitlinear_pack_kmajor", "bitlinear_ffn_sparse", "bitlinear_quant_act_a4", "bitlinear_forward_a4"):
         assert n in names
 
 
@@ -73,10 +73,11 @@ def test_op_numbering_matches_header():
     vals = {k: int(v) for k, v in re.findall(r"(BL_OP_\w+)\s*=\s*(\d+)", body)}
     assert vals == {"BL_OP_FORWARD": OP_FORWARD, "BL_OP_FFN": OP_FFN, "BL_OP_PACK": OP_PACK,
                     "BL_OP_GEMM_I32": OP_GEMM_I32, "BL_OP_PACK_THRESHOLD": OP_PACK_THRESHOLD,
-                    "BL_OP_FORWARD_NORM": OP_FORWARD_NORM, "BL_OP_FFN_SPARSE": OP_FFN_SPARSE}
+                    "BL_OP_FORWARD_NORM": OP_FORWARD_NORM, "BL_OP_FFN_SPARSE": OP_FFN_SPARSE,
+                    "BL_OP_FORWARD_A4": OP_FORWARD_A4}
     import bit_ternary_weight_bitlinear_amd as bl
     assert (bl.OP_FORWARD, bl.OP_FFN, bl.OP_PACK, bl.OP_GEMM_I32, bl.OP_PACK_THRESHOLD,
-            bl.OP_FORWARD_NORM, bl.OP_FFN_SPARSE) == (0, 1, 2, 3, 4, 5, 6)
+            bl.OP_FORWARD_NORM, bl.OP_FFN_SPARSE, bl.OP_FORWARD_A4) == tuple(range(8))
 
 
 def test_forward_argument_errors(lib):
@@ -163,6 +164,19 @@ def test_sparse_ffn_argument_errors(lib):
     assert f(A, 1, 1, 4104, 14336, A, A, A, A, A, A, A, None, None, A, need, None) == BL_ERR_SHAPE
     assert f(A, 1, 1, 4096, 14336, A, A, A, A, MIS, A, A, None, None, A, need, None) == BL_ERR_ALIGN
     assert f(A, 1, 1, 4096, 14336, A, A, A, A, A, A, A, None, None, A, need - 1, None) == BL_ERR_WORKSPACE
+
+
+def test_a4_argument_errors(lib):
+    qa = lib.bitlinear_quant_act_a4
+    assert qa(None, 1, 1, 256, 128, A, A, None) == BL_ERR_NULL
+    assert qa(A, 1, 1, 256, 0, A, A, None) == BL_ERR_VALUE
+    assert qa(A, 1, 1, 256, 257, A, A, None) == BL_ERR_VALUE
+    assert qa(A, 1, 1, 255, 128, A, A, None) == BL_ERR_SHAPE
+    fa = lib.bitlinear_forward_a4
+    need = lib.bitlinear_workspace_size(OP_FORWARD_A4, 1, 256, 8)
+    assert need >= 256 * 256
+    assert fa(A, 1, 1, 256, 0, A, A, 8, A, None, A, need, None) == BL_ERR_VALUE
+    assert fa(A, 1, 1, 256, 128, A, A, 8, A, None, A, need - 1, None) == BL_ERR_WORKSPACE
 
 
 def test_noalloc_argument_errors(lib):

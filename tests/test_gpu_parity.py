@@ -446,3 +446,52 @@ def test_ffn_sparse_all_zero_and_dense_h(bl):
     assert np.all(r["qh"] != 0)
     np.testing.assert_array_equal(host(hq), r["qh"])
     assert_y_close(host(y), r["y"])
+
+
+# ------------------------------------------------------------------ 4-bit activations (W1.58A4)
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k,keep", [(1, 4, 2), (3, 260, None), (4, 2560, None), (7, 6912, None), (5, 100, 1),
+                                      (2, 64, 64), (64, 4096, 1000), (2, 16388, None), (1027, 8196, None),
+                                      (2, 20000, 7)])
+def test_quant_act_a4_bit_exact(bl, dtype, m, k, keep):
+    x = synth.activations(180, m, k, dtype=dtype, outlier_channels=min(3, k), outlier_scale=30.0)
+    q, s = bl.quant_act_a4(to_dev(x, dtype), keep)
+    q_ref, s_ref = oracle.quant_act_a4(x, dtype, keep)
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+def test_quant_act_a4_hand_worked(bl, golden):
+    for c in golden["a4_cases"]:
+        q, s = bl.quant_act_a4(to_dev(np.array(c["x_f32"], np.float32)), c["keep"])
+        np.testing.assert_array_equal(host(q), c["q"], err_msg=c["name"])
+        np.testing.assert_array_equal(host(s), np.array(c["s"], np.float32))
+        if "w" in c:
+            packed, gamma = bl.pack_weights(to_dev(np.array(c["w"], np.float32)))
+            y, acc = bl.forward_a4(to_dev(np.array(c["x_f32"], np.float32)), packed, gamma, c["keep"],
+                                   return_acc=True)
+            np.testing.assert_array_equal(host(acc), c["acc"])
+            np.testing.assert_array_equal(host(y), np.array(c["y"], np.float32))
+
+
+def test_quant_act_a4_ties_everywhere(bl):
+    """Many equal magnitudes (bf16 rounding of small integers): every entry tied
+    with the threshold is kept on both sides."""
+    x = np.round(synth.activations(181, 16, 1024, dtype="f32") * 4).astype(np.float32)
+    q, s = bl.quant_act_a4(to_dev(x), 512)
+    q_ref, s_ref = oracle.quant_act_a4(x, "f32", 512)
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (1, 6912, 2560), (3, 260, 70), (8, 2560, 700),
+                                   (40, 6912, 300), (50, 14336, 64), (300, 2560, 256), (2048, 2560, 6912)])
+def test_forward_a4(bl, m, k, n):
+    w, p_ref, g_ref, _ = make_linear(182, 1, n, k)
+    x = synth.activations(182, m, k, dtype="bf16", heavy_channels=max(1, k // 100))
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward_a4(to_dev(x, "bf16"), packed, gamma, return_acc=True)
+    r = oracle.forward_a4(x, p_ref, g_ref, k, "bf16")
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
