@@ -7,10 +7,13 @@ hot path for that token: per-token int8 quantization (fused into the decode
 kernel's prologue), ternary x int8 product, rescale -- for both matrices.
 value = packed-weight bytes per step / step time (GB/s).
 
-Every other workload is measured in the same run and reported under "extra":
-the small M=4, 256x256 layer (latency), one 2B-class layer at 1/8/32/64 tokens
-(packed GB/s), prefill at 2048 tokens through the two FFN matrices (int8
-TOPS), and the 8B-class FFN block at 1 and 2048 tokens.
+Every other workload is measured in the same run: prefill at 2048 tokens
+through the two FFN matrices (int8 TOPS, "prefill"), and under "extra" the
+small M=4, 256x256 layer (latency), one 2B-class layer at 1/8/32/64 tokens
+(packed GB/s), the 8B-class FFN block at 1 and 2048 tokens (with the sparse
+down projection at one token), and the variants: the RMS norm fused into the
+quantization and 4-bit top-K activations on the decode and prefill shapes,
+the three activation quantizers alone, and the two weight quantizers.
 
 Cold weights: the packed matrices of the HBM-bound workloads rotate through a
 pool of distinct copies larger than 2x the 256 MB last-level cache, and before
@@ -402,6 +405,90 @@ def bench_ffn(bl, torch, dev, tm, steps, warmup, pool_mb):
     return out
 
 
+def bench_variants(bl, torch, dev, tm, steps, warmup, pool_mb):
+    """The other quantizers on the same shapes: the RMS norm fused into the
+    activation quantization, 4-bit top-K activations (W1.58A4), and the
+    threshold weight quantizer against the absmean one."""
+    out = {}
+    cfg = synth.WORKLOADS[2]
+    _, mats, xs = decode_inputs(bl, torch, dev)
+    pool, _ = rotation_pool(mats, pool_mb << 20)
+    P = len(pool)
+    packed_bytes = sum(p.numel() for p, _ in mats)
+    gains = [(1.0 + 0.25 * torch.randn(x.shape[1], device=dev)).float().contiguous() for x in xs]
+    wss = [torch.empty(max(bl.workspace_size(op, 1, k, n) for op in (bl.OP_FORWARD_NORM, bl.OP_FORWARD_A4)),
+                       dtype=torch.uint8, device=dev) for k, n in cfg["mats"]]
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for _, n in cfg["mats"]]
+    dec = {}
+    for name, fn in (("norm", lambda j, w: bl.forward_norm(xs[j], w[j][0], w[j][1], gains[j], out=ys[j],
+                                                          workspace=wss[j])),
+                     ("a4", lambda j, w: bl.forward_a4(xs[j], w[j][0], w[j][1], out=ys[j], workspace=wss[j]))):
+        def step(i, fn=fn):
+            w = pool[i % P]
+            fn(0, w)
+            fn(1, w)
+        for i in range(warmup):
+            step(P - 1 - (i % P))
+        t = tm.steps_region(step, steps, P)
+        dec[name] = dict(us_per_step=round(t * 1e6, 3), packed_gbs=round(packed_bytes / t / 1e9, 2),
+                         frac_of_hbm_peak=r4(packed_bytes / t / 1e9 / HBM_PEAK_GBS))
+    out["decode_m1_2560x6912_6912x2560"] = dec
+
+    c4 = synth.WORKLOADS[4]
+    m = c4["m"]
+    pre, quant = {}, {}
+    for (k, n), tid in zip(c4["mats"], ("up", "down")):
+        x = act_tensor(torch, 4, m, k, dev, heavy_channels=round(0.01 * k))
+        q = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sc = torch.empty(m, dtype=torch.float32, device=dev)
+        lib = bl.load_library()
+        stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+        calls = {"absmax_int8": lambda i: lib.bitlinear_quant_act(x.data_ptr(), 1, m, k, q.data_ptr(), sc.data_ptr(),
+                                                                   stream()),
+                 "rms_norm_int8": lambda i: lib.bitlinear_quant_act_norm(x.data_ptr(), 1, m, k, None, q.data_ptr(),
+                                                                         sc.data_ptr(), stream()),
+                 "topk_e2m1": lambda i: lib.bitlinear_quant_act_a4(x.data_ptr(), 1, m, k, (k + 1) // 2, q.data_ptr(),
+                                                                   sc.data_ptr(), stream())}
+        moved = m * k * 3  # bf16 in, int8 out
+        quant[f"k{k}"] = {name: dict(us=round(tm.launch_mean(c, 8, seconds=0.1) * 1e6, 2),
+                                     gbs=round(moved / tm.launch_mean(c, 8, seconds=0.1) / 1e9, 1))
+                          for name, c in calls.items()}
+        packed, gamma = make_weights(bl, torch, 4, tid, n, k, dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ws = torch.empty(bl.workspace_size(bl.OP_FORWARD_A4, m, k, n), dtype=torch.uint8, device=dev)
+        ops = 2.0 * m * n * k
+        pre[f"{k}x{n}"] = {}
+        for name, fn in (("norm", lambda i: bl.forward_norm(x, packed, gamma, out=y, workspace=ws)),
+                         ("a4", lambda i: bl.forward_a4(x, packed, gamma, out=y, workspace=ws))):
+            for _ in range(warmup):
+                fn(0)
+            t = tm.launch_mean(fn, 8, seconds=0.2)
+            pre[f"{k}x{n}"][name] = dict(us=round(t * 1e6, 2), tops=round(ops / t / 1e12, 1),
+                                         frac_of_int8_mfma_peak=r4(ops / t / 1e12 / INT8_MFMA_PEAK_TOPS))
+    out["prefill_m2048"] = pre
+    out["quantizers_m2048_us"] = quant
+
+    packs = {}
+    for n, k in ((6912, 2560), (14336, 4096)):
+        w = torch.from_numpy(weights(5 if n == 14336 else 2, "gate" if n == 14336 else "up", n, k)).to(dev)
+        pk = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+        g = torch.empty(4, dtype=torch.float32, device=dev)
+        wsb = torch.empty(bl.workspace_size(bl.OP_PACK_THRESHOLD, 0, k, n), dtype=torch.uint8, device=dev)
+        lib = bl.load_library()
+        ab = lambda i: lib.bitlinear_pack_weights(w.data_ptr(), n, k, pk.data_ptr(), g.data_ptr(),  # noqa: E731
+                                                  wsb.data_ptr(), wsb.numel(),
+                                                  torch.cuda.current_stream().cuda_stream)
+        th = lambda i: lib.bitlinear_pack_weights_threshold(w.data_ptr(), n, k, 0.7, pk.data_ptr(),  # noqa: E731
+                                                            g.data_ptr(), g[1:].data_ptr(), wsb.data_ptr(),
+                                                            wsb.numel(), torch.cuda.current_stream().cuda_stream)
+        ta, tt = tm.launch_mean(ab, 2, seconds=0.2), tm.launch_mean(th, 2, seconds=0.2)
+        packs[f"{n}x{k}"] = dict(absmean_us=round(ta * 1e6, 1), threshold_us=round(tt * 1e6, 1),
+                                 fp32_weight_mb=round(n * k * 4 / 1e6, 1))
+        del w
+    out["weight_pack_offline"] = packs
+    return out
+
+
 # --------------------------------------------------------------------------- profiling
 
 def profile_run(bl, torch, dev, what, steps, pool_mb):
@@ -628,6 +715,8 @@ def main():
     if not args.headline_only:
         extra["ffn_8b"] = bench_ffn(bl, torch, dev, tm, heavy_steps, heavy_warmup, args.pool_mb)
         log("ffn:", json.dumps(extra["ffn_8b"]))
+        extra["variants"] = bench_variants(bl, torch, dev, tm, args.steps, args.warmup, args.pool_mb)
+        log("variants:", json.dumps(extra["variants"]))
 
     algo = float(np.mean(dec["algo_bytes"]))
     kmean = float(np.mean(dec["kernel_s"]))
