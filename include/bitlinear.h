@@ -45,11 +45,21 @@ typedef enum {
     BL_ERR_DTYPE = 4,      /* unknown activation dtype                          */
     BL_ERR_WORKSPACE = 5,  /* workspace smaller than bitlinear_workspace_size() */
     BL_ERR_HIP = 6,        /* a kernel launch failed                            */
-    BL_ERR_VALUE = 7       /* a scalar argument is out of range                 */
+    BL_ERR_VALUE = 7,      /* a scalar argument is out of range                 */
+    /* range sentinels, never returned: every int32 is a value of the type, so
+       a caller may pass any int (the library reports unknown values) */
+    BL_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    BL_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } bl_status;
 
-/* Element type of the activation input x. */
-typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+/* Element type of the activation input x (other values: BL_ERR_DTYPE; the
+   sentinels make every int32 a value of the type). */
+typedef enum {
+    BL_F32 = 0,
+    BL_BF16 = 1,
+    BL_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    BL_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
+} bl_dtype;
 
 /* Operation selector for bitlinear_workspace_size(): 0 = forward, 1 = FFN, as
  * the two calls a layer makes per batch; the offline pack and the bare integer
