@@ -32,7 +32,7 @@ ceiling): once with the GEMV's grid and access pattern, once with the best
 grid found. `cpu_baseline` times the CPU oracle on bounded samples of every
 workload.
 
-`--profile decode|prefill|layer8|layer64|ffn1|ffn1sparse|ffn2048` runs one workload
+`--profile decode|prefill|layer8|layer64|ffn1|ffn1sparse|ffn2048|variants` runs one workload
 eagerly (no graphs, no JSON line) for profilers: --steps steps, then one plain
 256 MiB device copy whose HBM byte counters calibrate those of the kernels.
 """
@@ -541,6 +541,31 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
             for i in range(steps):
                 g, u, dt = tpool[i % len(tpool)]
                 bl.ffn_sparse(x, g, u, dt, workspace=ws)
+    elif what == "variants":
+        # the RMS-norm and 4-bit forwards (decode, cold weights; 2048 tokens),
+        # the threshold and absmean packs
+        cfg, mats, xs = decode_inputs(bl, torch, dev)
+        pool, _ = rotation_pool(mats, pool_mb << 20)
+        for i in range(steps):
+            ws = pool[i % len(pool)]
+            for j in range(2):
+                bl.forward_norm(xs[j], ws[j][0], ws[j][1])
+        for i in range(steps):
+            ws = pool[(i + steps) % len(pool)]
+            for j in range(2):
+                bl.forward_a4(xs[j], ws[j][0], ws[j][1])
+        c4 = synth.WORKLOADS[4]
+        for tid, (k, n) in zip(("up", "down"), c4["mats"]):
+            packed, gamma = make_weights(bl, torch, 4, tid, n, k, dev)
+            x = act_tensor(torch, 4, c4["m"], k, dev, heavy_channels=round(0.01 * k))
+            for i in range(max(1, steps // 10)):
+                bl.forward_norm(x, packed, gamma)
+                bl.forward_a4(x, packed, gamma)
+                bl.quant_act(x)
+        w = torch.from_numpy(weights(5, "gate", 14336, 4096)).to(dev)
+        for i in range(3):
+            bl.pack_weights(w)
+            bl.pack_weights_threshold(w, 0.7)
     elif what == "ffn2048":
         cfg = synth.WORKLOADS[5]
         hid, f, m = cfg["hidden"], cfg["ffn"], max(cfg["ms"])
@@ -679,7 +704,8 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn1sparse", "ffn2048"],
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn1sparse", "ffn2048",
+                                          "variants"],
                     default=None, help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()
 
