@@ -301,6 +301,13 @@ bl_status bitlinear_quant_act_norm(const void *x, bl_dtype dtype, int64_t m, int
 bl_status prequant_contraction(const FwdLayout &L, int64_t m, int64_t k, int64_t n, const uint8_t *w,
                                const float *gamma, float *y, int32_t *acc_out, float qmax, hipStream_t st)
 {
+    if (gemv_prequant_supported(m, L.kp)) {  // 1..4 tokens: the decode kernel
+        GemvProblem p{};
+        p.x = L.qp; p.bf16 = false; p.m = m; p.k = k; p.kp = L.kp; p.n = n;
+        p.w0 = w; p.ldw = L.kp / 4; p.gamma0 = gamma; p.out = y; p.acc_out = acc_out;
+        p.pre_s = L.s; p.pre_sumq = L.sumq; p.qmax = qmax;
+        return hip_status(launch_gemv(p, st));
+    }
     if (bgemv_prequant_supported(m, k)) {  // 5..64 tokens, k <= 8192
         GemvProblem bp{};
         bp.x = L.qp; bp.bf16 = false; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;

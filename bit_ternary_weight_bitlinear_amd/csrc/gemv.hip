@@ -48,6 +48,9 @@ struct GemvArgs {
     int8_t *q_out;
     float *s_out;
     float *hmax_part;   // gate/up pair only, optional: max |h| per (workgroup, token)
+    const float *pre_s;       // PREQ: the quantization kernel's scales and code sums
+    const int32_t *pre_sumq;
+    float qmax;               // code of the largest magnitude (127; 12 for doubled E2M1 codes)
     int rows_per_wg;  // R
     int chunks;       // kp / 64
 };
@@ -59,10 +62,13 @@ __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) &
 // RES: all m*ceil(k/16) activation groups fit in SL <= kSlots per thread
 // (loaded once, quantized from registers; SL is sized to the problem so that
 // unused slots hold no registers). FULL: k % 16 == 0. JM: (row, 8-chunk block)
-// units per lane group.
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots>
+// units per lane group. PREQ: x holds quantized rows [m][kp] in the qperm
+// order (with pre_s and pre_sumq) written by a quantization kernel: their
+// 16-byte words go to LDS as they are, one barrier, no quantization.
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
+    static_assert(!PREQ || (RES && FULL && !DUAL), "quantized rows: resident slots, one matrix");
     constexpr int NA = DUAL ? 2 : 1;
     extern __shared__ __align__(16) int8_t lds[];  // q [MT][kp], then int32 sums [NA][MT][R]
     __shared__ float red_f[MT][kGW];
@@ -76,8 +82,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     const int64_t r0 = (int64_t)blockIdx.x * R;
     const int rows = (int)((a.n - r0) < R ? (a.n - r0) : R);
     const T *x = static_cast<const T *>(a.x);
-    const int G = (int)ceil_div(a.k, 16);
     const int GP = (int)(a.kp / 16);
+    const int G = PREQ ? GP : (int)ceil_div(a.k, 16);  // quantized rows include their zero padding
     const int NG = MT * G;
 
     // 1. activation loads first: the quantization waits only for these. They
@@ -88,8 +94,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     //    the weights are requested: otherwise they queue behind the weights
     //    and the quantization ends later (measured: ~0.3 us per launch either
     //    way). Every slot is loaded (clamped to a valid group), with no branch.
-    constexpr bool kActFirst = JM * NA >= 6;
-    constexpr int XQ = (int)sizeof(T);  // 16-byte words per 16-input group (bf16: 2, fp32: 4)
+    constexpr bool kActFirst = JM * NA >= 6 && !PREQ;
+    constexpr int XQ = PREQ ? 1 : (int)sizeof(T);  // 16-byte words per 16-input group (bf16: 2, fp32: 4)
     uint4 xq[SL][XQ];
     int slot_t[SL], slot_g[SL];
     if constexpr (RES) {
@@ -98,7 +104,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
             const int f = min(tid + s * kGT, NG - 1);
             slot_t[s] = MT == 1 ? 0 : f / G;
             slot_g[s] = f - slot_t[s] * G;
-            const uint4 *p = reinterpret_cast<const uint4 *>(x + slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
+            const uint4 *p = PREQ ? reinterpret_cast<const uint4 *>(static_cast<const int8_t *>(a.x) +
+                                                                    slot_t[s] * a.kp + 16 * (int64_t)slot_g[s])
+                                  : reinterpret_cast<const uint4 *>(x + slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
 #pragma unroll
             for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
         }
@@ -153,13 +161,28 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. per-token absmax, then int8 codes into LDS in the qperm order
-    if constexpr (RES && !kActFirst) {
+    if constexpr (RES && !kActFirst && !PREQ) {
 #pragma unroll
         for (int s = 0; s < SL; ++s) unpack_group<T>(xq[s], xr[s]);
     }
     float st[MT], inv[MT];
     int sq[MT];
-    {
+    if constexpr (PREQ) {
+        // the quantized rows' words into LDS, their scales and sums from memory
+#pragma unroll
+        for (int s = 0; s < SL; ++s)
+            if (tid + s * kGT < NG)
+                *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * a.kp + lds_slot(slot_g[s] >> 2, slot_g[s] & 3)) =
+                    xq[s][0];
+        for (int i = tid; i < NA * MT * R; i += kGT) acc_lds[i] = 0;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            st[t] = a.pre_s[t];
+            inv[t] = 0.0f;
+            sq[t] = a.pre_sumq[t];
+        }
+        __syncthreads();
+    } else {
         float amax[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
@@ -328,8 +351,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     float hmax[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const float ca = token_scale(st[t], a.gamma0[0]);
-        const float cb = DUAL ? token_scale(st[t], a.gamma1[0]) : 0.0f;
+        const float ca = token_scale(st[t], a.gamma0[0], a.qmax);
+        const float cb = DUAL ? token_scale(st[t], a.gamma1[0], a.qmax) : 0.0f;
         hmax[t] = 0.0f;
         for (int r = tid; r < rows; r += kGT) {
             const int va = acc_lds[t * R + r] - sq[t];
@@ -407,10 +430,10 @@ bool gemv_supported(int64_t m, int64_t kp)
 
 namespace {
 
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots>
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false>
 void launch_one(dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL>), grid, dim3(kGT), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL, PREQ>), grid, dim3(kGT), lds, st, a);
 }
 
 // single token, whole groups, activations resident: the decode hot path, with
@@ -486,6 +509,35 @@ int64_t gemv_grid(int64_t n, int64_t kp, bool dual)
     return ceil_div(n, gemv_rows_per_wg(n, kp / 64, dual));
 }
 
+bool gemv_prequant_supported(int64_t m, int64_t kp)
+{
+    return gemv_supported(m, kp) && m * (kp / 16) <= (int64_t)kSlots * kGT;
+}
+
+namespace {
+
+template <int MT, int SL>
+void launch_preq_mt(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    if (jm <= 2) launch_one<int8_t, MT, false, true, true, 2, SL, true>(grid, lds, st, a);
+    else if (jm <= 4) launch_one<int8_t, MT, false, true, true, 4, SL, true>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<int8_t, MT, false, true, true, 8, SL, true>(grid, lds, st, a);
+    else launch_one<int8_t, MT, false, true, true, 16, SL, true>(grid, lds, st, a);
+}
+
+template <int SL>
+void launch_preq(int m, int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    switch (m) {
+    case 1: launch_preq_mt<1, SL>(jm, grid, lds, st, a); break;
+    case 2: launch_preq_mt<2, SL>(jm, grid, lds, st, a); break;
+    case 3: launch_preq_mt<3, SL>(jm, grid, lds, st, a); break;
+    default: launch_preq_mt<4, SL>(jm, grid, lds, st, a); break;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
 {
     GemvArgs a;
@@ -493,7 +545,7 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw;
     a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out; a.q_out = p.q_out; a.s_out = p.s_out;
-    a.hmax_part = p.hmax_part;
+    a.hmax_part = p.hmax_part; a.pre_s = p.pre_s; a.pre_sumq = p.pre_sumq; a.qmax = p.qmax;
     a.chunks = (int)(p.kp / 64);
     const bool dual = p.w1 != nullptr;
     const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);
@@ -501,6 +553,13 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     const int jm = (int)ceil_div(r * gemv_blocks(a.chunks), (int64_t)(kGT / 8));
     const dim3 grid((unsigned)ceil_div(p.n, r));
     const size_t lds = gemv_lds_bytes(p.m, p.kp, r, dual);
+    if (p.pre_s) {  // quantized rows (a quantization kernel ran first)
+        const int64_t sl = ceil_div(p.m * (p.kp / 16), (int64_t)kGT);
+        if (sl <= 1) launch_preq<1>((int)p.m, jm, grid, lds, st, a);
+        else if (sl <= 2) launch_preq<2>((int)p.m, jm, grid, lds, st, a);
+        else launch_preq<4>((int)p.m, jm, grid, lds, st, a);
+        return hipGetLastError();
+    }
     if (p.bf16) {
         if (dual) dispatch<bf16_t, true>(p, jm, grid, lds, st, a);
         else dispatch<bf16_t, false>(p, jm, grid, lds, st, a);

@@ -52,12 +52,14 @@ struct GemvProblem {
     int32_t *acc_out;        // optional (single matrix only)
     int8_t *q_out;           // optional natural int8 copy of the quantized activations
     float *s_out;            // optional per-token scales
-    const float *pre_s;      // 5..64-token kernel, mode 2 only (see bgemv_mode)
+    const float *pre_s;      // quantized rows: 5..64-token kernel mode 2, or the decode kernel
     const int32_t *pre_sumq;
     float qmax = 127.0f;     // mode 2: code of the largest magnitude (127 int8, 12 doubled E2M1)
     float *hmax_part;        // gate/up pair, optional: max |h| per (workgroup, token), [grid][m]
 };
 bool gemv_supported(int64_t m, int64_t kp);
+// the decode kernel on quantized rows (pre_s set: x holds qperm rows [m][kp])
+bool gemv_prequant_supported(int64_t m, int64_t kp);
 // workgroups of a decode launch (the number of hmax_part rows it writes)
 int64_t gemv_grid(int64_t n, int64_t kp, bool dual);
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
