@@ -28,11 +28,13 @@
 // 技术", paragraph on progressive quantization: MinMax FP4 with E2M1 bits, top-K
 // sparsification of 50 %). Per token, the keep-th largest magnitude tau is
 // found by a radix select on the fp32 bits of |x| (non-negative floats order
-// like their bit patterns), two bits per pass from the top, each pass counting
-// the candidates per digit and reducing the counts over the workgroup (no
-// atomics); entries with |x| >= tau are kept, v = x * (6 / s) with s =
-// max(max|x|, 1e-5), and v goes to the nearest E2M1 value (ties to the even
-// mantissa), stored doubled as an int8 code in [-12, 12].
+// like their bit patterns) with 11-bit digits from the top: each pass builds a
+// 2048-bin histogram of the candidates' digit in LDS, and every wave scans it
+// on its own for the digit that holds the keep-th largest (two passes for
+// bf16, whose low 16 bits are zero; three for fp32). Entries with |x| >= tau
+// are kept, v = x * (6 / s) with s = max(max|x|, 1e-5), and v goes to the
+// nearest E2M1 value (ties to the even mantissa), stored doubled as an int8
+// code in [-12, 12].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -152,25 +154,52 @@ __device__ inline int e2m1_doubled(float v)
     return v < 0.0f ? -c : c;
 }
 
-// three counts summed over the workgroup; red alternates between two halves
-// (parity) so one barrier per call suffices
-__device__ inline int3 block_sum3(int3 c, int (*red)[3][4], int parity)
+// inclusive prefix sum over the 64 lanes: Kogge-Stone steps of 1, 2, 4 and 8
+// inside each 16-lane row (row_shr, lanes with no source add 0), then the row
+// broadcasts carry each row's total into the rows above it
+__device__ inline int wave_scan(int v)
 {
-    c.x = wave_sum(c.x);
-    c.y = wave_sum(c.y);
-    c.z = wave_sum(c.z);
-    if ((threadIdx.x & 63) == 0) {
-        const int w = threadIdx.x >> 6;
-        red[parity][0][w] = c.x;
-        red[parity][1][w] = c.y;
-        red[parity][2][w] = c.z;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+    return v;
+}
+
+constexpr int kDigitBits = 11;
+constexpr int kDigitBins = 1 << kDigitBits;
+
+// The digit of the want-th largest candidate, from a histogram h of
+// kDigitBins bins (bins past the digit's range hold 0); want becomes the rank
+// of tau among the candidates that share that digit. Every wave computes it
+// alone, with no barrier: lane L sums bins 32L .. 32L+31 (read in a rotated
+// order to spread the LDS banks), a prefix sum over the lanes gives each lane
+// the count above its range and so the lane whose range holds the want-th
+// largest, and a second prefix sum over that lane's 32 bins gives the bin.
+__device__ inline uint32_t pick_digit(const int *h, int &want)
+{
+    const int lane = threadIdx.x & 63;
+    const int4 *hp = reinterpret_cast<const int4 *>(h + 32 * lane);
+    int sl = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int4 c = hp[(i + lane) & 7];
+        sl += c.x + c.y + c.z + c.w;
     }
-    __syncthreads();
-    int3 r;
-    r.x = red[parity][0][0] + red[parity][0][1] + red[parity][0][2] + red[parity][0][3];
-    r.y = red[parity][1][0] + red[parity][1][1] + red[parity][1][2] + red[parity][1][3];
-    r.z = red[parity][2][0] + red[parity][2][1] + red[parity][2][2] + red[parity][2][3];
-    return r;
+    const int pl = wave_scan(sl);
+    const int above = __builtin_amdgcn_readlane(pl, 63) - pl;  // candidates in the lanes above
+    const uint64_t b1 = __ballot(above < want && want <= above + sl);
+    const int ls = b1 ? __builtin_ctzll(b1) : 0;
+    const int base = __builtin_amdgcn_readlane(above, ls);
+    const int c = lane < 32 ? h[32 * ls + lane] : 0;
+    const int p2 = wave_scan(c);
+    const int ge = base + __builtin_amdgcn_readlane(p2, 31) - p2 + c;  // candidates with digit >= 32 ls + lane
+    const uint64_t b2 = __ballot(lane < 32 && ge >= want && ge - c < want);
+    const int lj = b2 ? __builtin_ctzll(b2) : 0;
+    want -= __builtin_amdgcn_readlane(ge - c, lj);
+    return (uint32_t)(32 * ls + lj);
 }
 
 }  // namespace
@@ -286,13 +315,18 @@ __global__ __launch_bounds__(256) void act_quant_a4_kernel(const T *__restrict__
                                                            int8_t *__restrict__ q_perm, float *__restrict__ s,
                                                            int32_t *__restrict__ sumq)
 {
+    constexpr int LOW = sizeof(T) == 2 ? 16 : 0;  // bf16: the low 16 bits are zero
+    constexpr int PASSES = (31 - LOW + kDigitBits - 1) / kDigitBits;
+    __shared__ __align__(16) int hist[PASSES][kDigitBins];
     __shared__ float red_f[4];
     __shared__ int red_i[4];
-    __shared__ int red3[2][3][4];
     const int64_t t = blockIdx.x;
     const T *row = x + t * k;
     const int64_t G = ceil_div(k, 16);
     const bool resident = G <= (int64_t)RG * kThreads;
+
+    for (int i = threadIdx.x; i < PASSES * kDigitBins / 4; i += kThreads)
+        reinterpret_cast<int4 *>(&hist[0][0])[i] = make_int4(0, 0, 0, 0);
 
     float v[RG][16];
     float amax = 0.0f;
@@ -316,24 +350,23 @@ __global__ __launch_bounds__(256) void act_quant_a4_kernel(const T *__restrict__
     }
     amax = block_max(amax, red_f);
 
-    // radix select of tau, the keep-th largest |x|, two bits per pass. Inputs
-    // past k (the zero padding of the last group) are not candidates.
-    constexpr int LOW = sizeof(T) == 2 ? 16 : 0;  // bf16: the low 16 bits are zero
+    // radix select of tau, the keep-th largest |x|: bits 30..20, then 19..16
+    // for bf16 (19..9 and 8..0 for fp32). Inputs past k (the zero padding of
+    // the last group) are not candidates. The barrier in block_max above also
+    // publishes the zeroed histograms.
     uint32_t prefix = 0, pmask = 0;
     int want = (int)keep;
-    int parity = 0;
-    for (int b = 30; b >= LOW; b -= 2) {
-        int3 c = make_int3(0, 0, 0);  // candidates with digit >= 1, >= 2, == 3
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int hi = 31 - p * kDigitBits;
+        const int lo = hi - kDigitBits > LOW ? hi - kDigitBits : LOW;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        int *h = hist[p];
         auto count = [&](const float f[16], int64_t g) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const uint32_t key = __float_as_uint(fabsf(f[j]));
-                if ((FULL || 16 * g + j < k) && (key & pmask) == prefix) {
-                    const uint32_t d = (key >> b) & 3u;
-                    c.x += d >= 1u;
-                    c.y += d >= 2u;
-                    c.z += d == 3u;
-                }
+                if ((FULL || 16 * g + j < k) && (key & pmask) == prefix) atomicAdd(&h[(key >> lo) & dmask], 1);
             }
         };
         if (resident) {
@@ -349,15 +382,9 @@ __global__ __launch_bounds__(256) void act_quant_a4_kernel(const T *__restrict__
                 count(f, g);
             }
         }
-        const int3 tot = block_sum3(c, red3, parity);
-        parity ^= 1;
-        uint32_t d;
-        if (tot.z >= want) d = 3u;
-        else if (tot.y >= want) { d = 2u; want -= tot.z; }
-        else if (tot.x >= want) { d = 1u; want -= tot.y; }
-        else { d = 0u; want -= tot.x; }
-        prefix |= d << b;
-        pmask |= 3u << b;
+        __syncthreads();
+        prefix |= pick_digit(h, want) << lo;
+        pmask |= dmask << lo;
     }
     const uint32_t tau = prefix;  // the keep-th largest |x| (as bits)
     const float st = fmaxf(amax, kEps);
