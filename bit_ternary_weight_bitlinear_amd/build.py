@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
 BENCH_LIB = os.path.join(HERE, "libbitlinear_bench.so")
 SOURCES = ["api.hip", "pack.hip", "act_quant.hip", "gemv.hip", "bgemv.hip", "gemm.hip", "skinny.hip",
-           "sparse_down.hip"]
+           "sparse_down.hip", "bmma.hip"]
 BENCH_SOURCES = ["bench_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

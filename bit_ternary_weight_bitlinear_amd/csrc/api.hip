@@ -308,13 +308,6 @@ bl_status prequant_contraction(const FwdLayout &L, int64_t m, int64_t k, int64_t
         p.pre_s = L.s; p.pre_sumq = L.sumq; p.qmax = qmax;
         return hip_status(launch_gemv(p, st));
     }
-    if (bgemv_prequant_supported(m, k)) {  // 5..64 tokens, k <= 8192
-        GemvProblem bp{};
-        bp.x = L.qp; bp.bf16 = false; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
-        bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma; bp.out = y; bp.acc_out = acc_out;
-        bp.pre_s = L.s; bp.pre_sumq = L.sumq; bp.qmax = qmax;
-        return hip_status(launch_bgemv(bp, st));
-    }
     GemmProblem g{};
     g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;
@@ -408,10 +401,6 @@ bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
         return hip_status(launch_bgemv(bp, st));
     if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, k, L.kp, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
-    if (bmode == 2) {  // 5..64 tokens, quantized rows from the kernel above
-        bp.x = L.qp; bp.pre_s = L.s; bp.pre_sumq = L.sumq;
-        return hip_status(launch_bgemv(bp, st));
-    }
     GemmProblem g{};
     g.qp = L.qp; g.kp = L.kp; g.s = L.s; g.sumq = L.sumq; g.m = m; g.n = n;
     g.w0 = w; g.w1 = nullptr; g.ldw = L.kp / 4; g.gamma0 = gamma; g.gamma1 = nullptr;

@@ -342,9 +342,8 @@ template <typename T, int RB, int JM, int SL, bool PREQ, int MB>
 hipError_t bg_launch(dim3 grid, size_t lds, hipStream_t st, const BgemvArgs &a)
 {
     auto kern = bgemv_kernel<T, RB, JM, SL, PREQ, MB>;
-    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
-        return e;
+    static LdsLimit lim;
+    if (hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds, lim)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kBT), lds, st, a);
     return hipGetLastError();
 }

@@ -16,6 +16,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -105,6 +108,86 @@ __device__ inline int wave_sum(int v)
     v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
     v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
     return __builtin_amdgcn_readlane(v, 63);
+}
+
+// ---------------------------------------------------------------- dynamic LDS limit (host)
+// A launch with more dynamic LDS than the default limit needs the function's
+// limit raised (hipFuncSetAttribute, per function and device). Each launching
+// template instance keeps one LdsLimit; the attribute call happens only when a
+// device first needs more than it was given, not on every launch.
+struct LdsLimit {
+    static constexpr int kDevices = 64;
+    std::atomic<int> bytes[kDevices] = {};
+    std::mutex mu;
+};
+inline hipError_t allow_dynamic_lds(const void *kern, int bytes, LdsLimit &lim)
+{
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) return e;
+    if (dev < 0 || dev >= LdsLimit::kDevices)
+        return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (lim.bytes[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+    std::lock_guard<std::mutex> g(lim.mu);
+    const int have = lim.bytes[dev].load(std::memory_order_relaxed);
+    if (have >= bytes) return hipSuccess;
+    if (hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) return e;
+    lim.bytes[dev].store(bytes, std::memory_order_release);
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------- direct loads into LDS
+// Direct loads from global memory into LDS with a scalar base address and a
+// per-lane 32-bit byte offset. Lane i of the wave writes LDS byte address
+// lds + 16*i (lds + 4*i for the dword form); lds must be wave-uniform. Issued
+// as inline asm so that the only waits on these loads are the explicit ones in
+// ring_barrier(): the compiler would otherwise drain every in-flight direct
+// load before any LDS read. No VGPR is written by them.
+// a wave-uniform 64-bit address as a scalar operand
+__device__ inline uint64_t uniform_ptr(const void *p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline void dma16(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+__device__ inline void dma4(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+// LDS byte address of a pointer into the workgroup's LDS
+__device__ inline uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// s_waitcnt immediate: vmcnt <= VM, lgkmcnt <= LG, expcnt untouched (gfx9 encoding)
+template <int VM, int LG>
+constexpr int waitcnt_vm_lgkm() { return (VM & 15) | (7 << 4) | (LG << 8) | ((VM >> 4) << 14); }
+
+// Barrier that leaves the newest VM direct loads and the newest LG LDS reads
+// in flight: wait until at most VM vector-memory and LG LDS operations of this
+// thread are outstanding (both complete in issue order), then s_barrier. The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int VM, int LG = 0>
+__device__ inline void ring_barrier()
+{
+    static_assert(VM < 64 && LG < 16, "waitcnt fields");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm<VM, LG>());
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------- activation loads

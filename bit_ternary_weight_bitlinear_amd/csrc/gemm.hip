@@ -61,60 +61,6 @@ struct GemmArgs {
 // byte offset of (row, 16-byte group g) in a 64-byte-row LDS tile
 __device__ inline int tile_off(int row, int g) { return row * 64 + ((g ^ ((row >> 2) & 3)) << 4); }
 
-// Direct loads from global memory into LDS with a scalar base address and a
-// per-lane 32-bit byte offset. Lane i of the wave writes LDS byte address
-// lds + 16*i (lds + 4*i for the dword form); lds must be wave-uniform. Issued
-// as inline asm so that the only waits on these loads are the explicit ones in
-// ring_barrier(): the compiler would otherwise drain every in-flight direct
-// load before any LDS read. No VGPR is written by them.
-// a wave-uniform 64-bit address as a scalar operand
-__device__ inline uint64_t uniform_ptr(const void *p)
-{
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ inline void dma16(const void *sbase, uint32_t voff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
-}
-__device__ inline void dma4(const void *sbase, uint32_t voff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-                 :
-                 : "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory", "m0");
-}
-
-// LDS byte address of a pointer into the workgroup's LDS
-__device__ inline uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// s_waitcnt immediate: vmcnt <= VM, lgkmcnt <= LG, expcnt untouched (gfx9 encoding)
-template <int VM, int LG>
-constexpr int waitcnt_vm_lgkm() { return (VM & 15) | (7 << 4) | (LG << 8) | ((VM >> 4) << 14); }
-
-// Barrier that leaves the newest VM direct loads and the newest LG LDS reads
-// in flight: wait until at most VM vector-memory and LG LDS operations of this
-// thread are outstanding (both complete in issue order), then s_barrier. The
-// empty asm statements keep the compiler from moving memory accesses across.
-template <int VM, int LG = 0>
-__device__ inline void ring_barrier()
-{
-    static_assert(VM < 64 && LG < 16, "waitcnt fields");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm<VM, LG>());
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // one v_lshrrev_b64 (written out: the compiler would split a 64-bit shift whose
@@ -475,9 +421,8 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t st)
     a.n_tiles = (int)ceil_div(a.n, 32 * FN);
     a.m_tiles = (int)ceil_div(a.m, 128 * FM);
     const auto kern = gemm_kernel<FM, FN, EPI, DB, SPB>;
-    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
-        return e;
+    static LdsLimit lim;
+    if (hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds, lim)) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_tiles * a.m_tiles)), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }

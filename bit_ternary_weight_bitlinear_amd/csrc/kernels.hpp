@@ -115,9 +115,17 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t st);
 bool skinny_supported(int64_t m);
 hipError_t launch_skinny(const GemmProblem &p, hipStream_t st);
 
-// MFMA path for m tokens: the skinny kernel up to 64 tokens, the tiled GEMM above
+// ---- 1..64 tokens: row-tile x token-slice MFMA kernel with operands read
+// straight into registers (bmma.hip), same problem description; rows of up to
+// 16384 inputs (8192 for the gated pair)
+bool bmma_supported(int64_t m, int64_t kp, bool dual);
+hipError_t launch_bmma(const GemmProblem &p, hipStream_t st);
+
+// MFMA path for m tokens: bmma up to 64 tokens (the skinny kernel for longer
+// rows), the tiled GEMM above
 inline hipError_t launch_contraction(const GemmProblem &p, hipStream_t st)
 {
+    if (bmma_supported(p.m, p.kp, p.epi == EPI_GATE)) return launch_bmma(p, st);
     return skinny_supported(p.m) ? launch_skinny(p, st) : launch_gemm(p, st);
 }
 
