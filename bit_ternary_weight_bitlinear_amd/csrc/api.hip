@@ -392,13 +392,13 @@ bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
         p.out = y; p.acc_out = acc_out;
         return hip_status(launch_gemv(p, st));
     }
-    const int bmode = bgemv_mode(m, k, dtype == BL_BF16);
-    GemvProblem bp{};
-    bp.x = x; bp.bf16 = dtype == BL_BF16; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
-    bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma;
-    bp.out = y; bp.acc_out = acc_out;
-    if (bmode == 1)  // 5..16 tokens: quantization, products and rescale in one launch
+    if (bgemv_supported(m, k, dtype == BL_BF16)) {  // 5..16 tokens: quantization, products and rescale in one launch
+        GemvProblem bp{};
+        bp.x = x; bp.bf16 = dtype == BL_BF16; bp.m = m; bp.k = k; bp.kp = L.kp; bp.n = n;
+        bp.w0 = w; bp.ldw = L.kp / 4; bp.gamma0 = gamma;
+        bp.out = y; bp.acc_out = acc_out;
         return hip_status(launch_bgemv(bp, st));
+    }
     if (hipError_t e = launch_act_quant(x, dtype == BL_BF16, m, k, L.kp, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
     GemmProblem g{};

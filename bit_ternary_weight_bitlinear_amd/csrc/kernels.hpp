@@ -52,7 +52,7 @@ struct GemvProblem {
     int32_t *acc_out;        // optional (single matrix only)
     int8_t *q_out;           // optional natural int8 copy of the quantized activations
     float *s_out;            // optional per-token scales
-    const float *pre_s;      // quantized rows: 5..64-token kernel mode 2, or the decode kernel
+    const float *pre_s;      // quantized rows (the decode kernel): x holds qperm rows [m][kp]
     const int32_t *pre_sumq;
     float qmax = 127.0f;     // mode 2: code of the largest magnitude (127 int8, 12 doubled E2M1)
     float *hmax_part;        // gate/up pair, optional: max |h| per (workgroup, token), [grid][m]
@@ -63,13 +63,9 @@ bool gemv_prequant_supported(int64_t m, int64_t kp);
 // workgroups of a decode launch (the number of hmax_part rows it writes)
 int64_t gemv_grid(int64_t n, int64_t kp, bool dual);
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
-// 5..64 tokens, single matrix, k <= 8192. Mode 1 (up to 16 tokens):
-// quantization inside the launch; mode 2: x holds the qperm int8 rows
-// [m][kp] of the quantization kernel and pre_s / pre_sumq its scales and
-// sums; 0: neither (too many inputs for registers or LDS).
-int bgemv_mode(int64_t m, int64_t k, bool bf16);
-// whether the 5..64-token kernel takes these m, k with quantized rows (mode 2)
-bool bgemv_prequant_supported(int64_t m, int64_t k);
+// 5..16 tokens, single matrix, k <= 8192 (k % 16 == 0, m * k <= 32768):
+// quantization, products and rescale in one launch (bgemv.hip)
+bool bgemv_supported(int64_t m, int64_t k, bool bf16);
 hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st);
 
 // ---- decode FFN down projection over the input-major weights, skipping the
