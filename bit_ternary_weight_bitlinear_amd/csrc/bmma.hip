@@ -114,7 +114,9 @@ __global__ __launch_bounds__(kBmT) void bmma_kernel(BmmaArgs a)
 
     // 1. the token rows of this wave's quads into its LDS: load i of quad j
     //    covers tokens 4i..4i+3 (16 lanes each); slot p of token t holds its
-    //    piece (p - t) mod 16 of the quad. Quads past the range are not loaded.
+    //    piece (p - t) mod 16 of the quad. Quads past the range, and loads
+    //    whose four tokens are all past the tile's last token, are not issued
+    //    (the products of those LDS slots belong to tokens that are dropped).
     {
         const uint32_t wl0 = lds_addr(wl);
         const int8_t *base = a.qp + t0 * a.kp;
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(kBmT) void bmma_kernel(BmmaArgs a)
             const int q = qb + j;
 #pragma unroll
             for (int i = 0; i < 4 * TB; ++i) {
+                if (4 * i >= toks) break;  // uniform: rows past the tile's tokens are not needed
                 const int t = 4 * i + (lane >> 4);
                 const int src = (p - t) & 15;
                 // pieces past the row (the last quad of a row whose chunk
