@@ -32,7 +32,7 @@ ceiling): once with the GEMV's grid and access pattern, once with the best
 grid found. `cpu_baseline` times the CPU oracle on bounded samples of every
 workload.
 
-`--profile decode|prefill|layer8|layer64|ffn1|ffn1sparse|ffn2048|variants` runs one workload
+`--profile decode|prefill|layer8|layer32|layer64|ffn1|ffn1sparse|ffn2048|variants` runs one workload
 eagerly (no graphs, no JSON line) for profilers: --steps steps, then one plain
 256 MiB device copy whose HBM byte counters calibrate those of the kernels.
 """
@@ -509,9 +509,9 @@ def profile_run(bl, torch, dev, what, steps, pool_mb):
         for i in range(steps):
             for j in range(2):
                 rd.linear(pool[(i + 2 * steps) % len(pool)][j][0], 1024, 256)
-    elif what in ("layer8", "layer64"):
+    elif what in ("layer8", "layer32", "layer64"):
         cfg = synth.WORKLOADS[3]
-        m = 8 if what == "layer8" else 64
+        m = int(what[len("layer"):])
         mats = [make_weights(bl, torch, 3, tid, n, k, dev)
                 for tid, (k, n) in zip(("qkv", "o", "gate", "up", "down"), cfg["mats"])]
         pool, _ = rotation_pool(mats, pool_mb << 20)
@@ -704,7 +704,7 @@ def main():
     ap.add_argument("--pool-mb", type=int, default=640, help="rotation pool of packed weights (MB)")
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer64", "ffn1", "ffn1sparse", "ffn2048",
+    ap.add_argument("--profile", choices=["decode", "prefill", "layer8", "layer32", "layer64", "ffn1", "ffn1sparse", "ffn2048",
                                           "variants"],
                     default=None, help="eager launches for a profiler; prints no JSON line")
     args = ap.parse_args()

@@ -254,13 +254,10 @@ struct BmmaShape {
     int rb = 0, tb = 0, ts = 0, nq = 0;
 };
 
-// quads per wave (ceil(C / 32)) rounded up to an instantiated count (1, 2, 3,
-// 4, 6, 8); longer rows keep their count, which no instance takes
-int64_t bmma_nq(int64_t C)
-{
-    const int64_t q = ceil_div(C, (int64_t)(4 * kBmW));
-    return q <= 4 ? q : q <= 6 ? 6 : q <= 8 ? 8 : q;
-}
+// quads per wave: ceil(C / 32). At most 4 fit (8 waves x 4 quads x 16 tokens x
+// 256 bytes of LDS), i.e. rows of up to 8192 inputs; longer ones go to the
+// skinny kernel.
+int64_t bmma_nq(int64_t C) { return ceil_div(C, (int64_t)(4 * kBmW)); }
 
 // The tile for m tokens, n rows, kp inputs: among RB in {1, 2, 4} and TB in
 // 1..4 (TS = ceil(m / 16 TB) token slices), the one whose busiest CU takes
@@ -326,8 +323,6 @@ hipError_t bm_nq(int nq, const BmmaArgs &a, int epi, dim3 grid, hipStream_t st)
     case 2: return bm_epi<RB, TB, 2>(a, epi, grid, st);
     case 3: return bm_epi<RB, TB, 3>(a, epi, grid, st);
     case 4: return bm_epi<RB, TB, 4>(a, epi, grid, st);
-    case 6: return bm_epi<RB, TB, 6>(a, epi, grid, st);
-    case 8: return bm_epi<RB, TB, 8>(a, epi, grid, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -350,7 +345,7 @@ bool bmma_supported(int64_t m, int64_t kp, bool dual)
 {
     if (m < 1 || m > 64 || kp < 64) return false;
     const int64_t nq = bmma_nq(kp / 64);
-    return nq <= 8 && bmma_fits(1, 1, (int)nq, dual ? 2 : 1);
+    return nq <= 4 && bmma_fits(1, 1, (int)nq, dual ? 2 : 1);
 }
 
 hipError_t launch_bmma(const GemmProblem &p, hipStream_t st)

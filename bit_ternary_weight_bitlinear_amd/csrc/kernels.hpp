@@ -111,9 +111,9 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t st);
 bool skinny_supported(int64_t m);
 hipError_t launch_skinny(const GemmProblem &p, hipStream_t st);
 
-// ---- 1..64 tokens: row-tile x token-slice MFMA kernel with operands read
-// straight into registers (bmma.hip), same problem description; rows of up to
-// 16384 inputs (8192 for the gated pair)
+// ---- 1..64 tokens: row-tile x token-slice MFMA kernel with the token rows
+// staged per wave in LDS (bmma.hip), same problem description; rows of up to
+// 8192 inputs
 bool bmma_supported(int64_t m, int64_t kp, bool dual);
 hipError_t launch_bmma(const GemmProblem &p, hipStream_t st);
 

@@ -135,6 +135,47 @@ def test_gemm_i32_bit_exact(bl):
         np.testing.assert_array_equal(host(acc), q.astype(np.int64) @ wt.astype(np.int64).T)
 
 
+# The 1..64-token kernel on quantized rows (bmma) owns tiles of RB 16-row
+# blocks x TB 16-token blocks, splits the tokens over TS workgroups and gives
+# each of its 8 waves NQ quads of 64-input chunks; the shapes below reach
+# every RB in {1, 2, 4} and TB in {1..4} with ragged rows, tokens and chunk
+# quads (the tile the kernel's cost model picks is noted per shape).
+BMMA_SHAPES = [
+    (17, 260, 4100),    # RB 2, TB 2; 5 chunks (a partial quad); 4100 % 32 = 4 rows in the last tile
+    (33, 1100, 10000),  # RB 4, TB 3; 18 chunks
+    (49, 1000, 4100),   # RB 4, TB 2, two token slices
+    (49, 1000, 10000),  # RB 4, TB 4
+    (17, 2600, 10000),  # RB 4, TB 2, two quads per wave; 41 chunks
+    (64, 6912, 2561),   # RB 4, TB 1, four token slices, four quads per wave; one row in the last tile
+    (33, 260, 6913),    # RB 2, TB 3
+    (5, 8192, 300),     # RB 1, TB 1, 5 tokens (too many inputs for the one-launch kernel)
+    (40, 4100, 1000),   # RB 1, TB 1, three token slices, three quads per wave; 65 chunks
+    (57, 1100, 4099),   # RB 4, TB 2, two token slices; 3 rows in the last tile
+    (20, 5000, 6000),   # RB 4, TB 1, two token slices, three quads per wave; 79 chunks
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k,n", BMMA_SHAPES)
+def test_forward_bmma_tiles(bl, dtype, m, k, n):
+    w, p_ref, g_ref, _ = make_linear(93, 1, n, k)
+    x = synth.activations(93, m, k, dtype=dtype, outlier_channels=2, outlier_scale=20.0)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward(to_dev(x, dtype), packed, gamma, return_acc=True)
+    r = oracle.forward(x, p_ref, g_ref, k, dtype)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
+
+
+@pytest.mark.parametrize("m,k,n", [(33, 1100, 10000), (20, 5000, 6000), (49, 1000, 4100)])
+def test_gemm_i32_bmma_tiles(bl, m, k, n):
+    rng = np.random.default_rng(m * 7919 + k)
+    q = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    w, p_ref, _, wt = make_linear(95, 1, n, k)
+    acc = bl.gemm_i32(to_dev(q), to_dev(p_ref))
+    np.testing.assert_array_equal(host(acc), q.astype(np.int64) @ wt.astype(np.int64).T)
+
+
 # the largest sizes the boundary accepts (BL_MAX_DIM = 2^20 inputs or outputs,
 # BL_MAX_TOKENS = 2^22 tokens), each with the other dimensions small
 MAX_SHAPES = [(2, 1 << 20, 5), (1, 20, 1 << 20), (1 << 22, 4, 3)]
@@ -252,6 +293,13 @@ def _ffn_case(bl, cfg, m, hid, f, dtype="bf16"):
                                      (2, 8, 1 << 20)])  # the largest ffn width the boundary accepts
 def test_ffn_small(bl, m, hid, f):
     _ffn_case(bl, 96, m, hid, f)
+
+
+# the gate/up pair on bmma (two weight streams per tile): RB 2 with TB 2, 4
+# and 3, and RB 1 with two token slices; the down projections on RB 1 / 2
+@pytest.mark.parametrize("m,hid,f", [(17, 260, 4100), (49, 1000, 4100), (33, 1100, 6916), (24, 2600, 2000)])
+def test_ffn_bmma_tiles(bl, m, hid, f):
+    _ffn_case(bl, 97, m, hid, f)
 
 
 def test_ffn_hand_worked(bl, golden):
