@@ -146,11 +146,16 @@ __device__ inline void normalize_group(float f[16], float r, const float *gain, 
 
 // The nearest E2M1 value of v (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives),
 // doubled; at a midpoint the value with mantissa bit 0 (0, 1, 2, 4) wins.
+// The E2M1 values step by 0.5 below 2, by 1 below 4 and by 2 above, so the
+// doubled code is rint(|v| * 2 / d) * d with d = 1, 2, 4 in those ranges
+// (|v| times a power of two is exact, and rint's ties to even are exactly the
+// midpoint rule), capped at 12: no branches, and NaN gives 12.
 __device__ inline int e2m1_doubled(float v)
 {
     const float a = fabsf(v);
-    const int c = a <= 0.25f ? 0 : a < 0.75f ? 1 : a <= 1.25f ? 2 : a < 1.75f ? 3 : a <= 2.5f ? 4 : a < 3.5f ? 6
-                : a <= 5.0f ? 8 : 12;
+    const float up = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    const float d = a < 2.0f ? 1.0f : (a < 4.0f ? 2.0f : 4.0f);
+    const int c = (int)fminf(rintf(a * up) * d, 12.0f);
     return v < 0.0f ? -c : c;
 }
 
