@@ -533,6 +533,24 @@ def test_quant_act_a4_ties_everywhere(bl):
     np.testing.assert_array_equal(host(s), s_ref)
 
 
+def test_quant_act_a4_e2m1_rounding_edges(bl):
+    """With the row's absmax at 6 the E2M1 input is x itself: every midpoint of
+    the grid with both signs, the floats just below and above each midpoint,
+    the grid values and a few points near them, all kept."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(7)), grid,
+                           np.float32([5.999, 4.999, 0.001])])
+    row = np.concatenate([vals, -vals, np.float32([6.0])]).astype(np.float32)
+    row = np.concatenate([row, np.zeros((-len(row)) % 4, np.float32)])
+    x = np.stack([row, row[::-1].copy()])
+    q, s = bl.quant_act_a4(to_dev(x), x.shape[1])
+    q_ref, s_ref = oracle.quant_act_a4(x, "f32", x.shape[1])
+    assert np.all(s_ref == 6.0)
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
 @pytest.mark.parametrize("m,k,n", [(1, 2560, 6912), (1, 6912, 2560), (3, 260, 70), (8, 2560, 700),
                                    (40, 6912, 300), (50, 14336, 64), (300, 2560, 256), (2048, 2560, 6912)])
 def test_forward_a4(bl, m, k, n):
