@@ -76,6 +76,23 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     int8_t *q_lds = lds;
     int *acc_lds = reinterpret_cast<int *>(lds + MT * a.kp);
 
+    // the scalars of the later phases are requested here, before the
+    // activation loads: fetched where they are used, the kernel-argument line
+    // with the output pointers missed the scalar cache inside the quantization
+    // and gamma took an L2 round trip between the last barrier and the stores
+    const float g0 = a.gamma0[0];
+    const float g1 = DUAL ? a.gamma1[0] : 0.0f;
+    float pre_st[MT];
+    int pre_sq[MT];
+    if constexpr (PREQ) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            pre_st[t] = a.pre_s[t];
+            pre_sq[t] = a.pre_sumq[t];
+        }
+    }
+    asm volatile("" ::"s"(a.out), "s"(a.acc_out), "s"(a.q_out), "s"(a.s_out), "s"(a.hmax_part), "s"(a.qmax));
+
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int R = a.rows_per_wg, C = a.chunks;
@@ -159,6 +176,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     // keep every load above this point in issue order: nothing below may be
     // hoisted between them, so all of this thread's reads are in flight at once
     __builtin_amdgcn_sched_barrier(0);
+    // gamma is needed from here on (it has long arrived): without this use the
+    // load sinks to the first barrier, whose wait then includes its latency
+    asm volatile("" ::"s"(g0), "s"(g1));
 
     // 3. per-token absmax, then int8 codes into LDS in the qperm order
     if constexpr (RES && !kActFirst && !PREQ) {
@@ -177,9 +197,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         for (int i = tid; i < NA * MT * R; i += kGT) acc_lds[i] = 0;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            st[t] = a.pre_s[t];
+            st[t] = pre_st[t];
             inv[t] = 0.0f;
-            sq[t] = a.pre_sumq[t];
+            sq[t] = pre_sq[t];
         }
         __syncthreads();
     } else {
@@ -351,8 +371,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
     float hmax[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const float ca = token_scale(st[t], a.gamma0[0], a.qmax);
-        const float cb = DUAL ? token_scale(st[t], a.gamma1[0], a.qmax) : 0.0f;
+        const float ca = token_scale(st[t], g0, a.qmax);
+        const float cb = DUAL ? token_scale(st[t], g1, a.qmax) : 0.0f;
         hmax[t] = 0.0f;
         for (int r = tid; r < rows; r += kGT) {
             const int va = acc_lds[t * R + r] - sq[t];
