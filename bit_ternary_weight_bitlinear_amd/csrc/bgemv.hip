@@ -80,6 +80,10 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     const T *x = static_cast<const T *>(a.x);
     const int G = (int)(a.k / 16);  // k % 16 == 0
     const int NG = M * G;
+    // gamma is requested now and waited for after the loads are out (fetched
+    // in the epilogue it put an L2 round trip between the last barrier and
+    // the stores)
+    const float gam = a.gamma[0];
 
     if (tid < kBMaxTok) {
         tok_max[tid] = 0u;
@@ -122,6 +126,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         // issue order = use order, so each quad waits only for its own load
         __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("" ::"s"(gam));
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
         slot_t[s] = slot_f[s] / G;
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 #pragma unroll
             for (int w = eb; w < kBW; w += RB) va += part[(w * 4 + v) * 64 + el];
             const int64_t o = (int64_t)t * a.n + r0 + row;
-            a.out[o] = (float)va * token_scale(tok_s[t], a.gamma[0], a.qmax);
+            a.out[o] = (float)va * token_scale(tok_s[t], gam, a.qmax);
             if (a.acc_out) a.acc_out[o] = va;
         }
     }

@@ -62,6 +62,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
     const uint8_t *wrow0 = a.w0 + row * a.ldw;
     const uint8_t *wrow1 = (DUAL ? a.w1 : a.w0) + row * a.ldw;
 
+    // the epilogue's operands, requested before the weights: read after the
+    // barrier they put an L2 round trip in front of the stores. Wave w's
+    // epilogue covers token block w (MB <= 4), token 16 w + lane % 16.
+    static_assert(MB <= 4, "one token block per wave in the epilogue");
+    const int64_t me = wave * 16 + lr;
+    int e_sq = 0;
+    float e_s = 0.0f;
+    if (wave < MB && me < a.m) {
+        e_sq = a.sumq[me];
+        if constexpr (EPI != EPI_ACC) e_s = a.s[me];
+    }
+    const float g0 = EPI != EPI_ACC ? a.gamma0[0] : 0.0f;
+    const float g1 = DUAL ? a.gamma1[0] : 0.0f;
+
     // two blocks in flight per wave: loads of block b+4 are issued before block b is used
     auto load_block = [&](int b, v4u wv[NA], v4i qv[4][MB]) {
         const int c = 4 * b + lh;
@@ -91,6 +105,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
 #pragma unroll
         for (int i = 0; i < KB; ++i) load_block(wave + 4 * i, wv[i], i == 0 ? qa : qb);
         __builtin_amdgcn_sched_barrier(0);  // keep every request ahead of the first use
+        asm volatile("" ::"s"(g0), "s"(g1));  // gamma fetched by now, not sunk to the epilogue
 #pragma unroll
         for (int i = 0; i < KB; ++i) {
             v4i (&qc)[4][MB] = (i & 1) ? qb : qa;
@@ -114,6 +129,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
     v4i qcur[4][MB], qnxt[4][MB];
     int b = wave;
     if (b < nblk) load_block(b, wcur, qcur);
+    asm volatile("" ::"s"(g0), "s"(g1));  // gamma fetched by now, not sunk to the epilogue
     while (b < nblk) {
         const int bn = b + 4;
         if (bn < nblk) load_block(bn, wnxt, qnxt);
@@ -151,12 +167,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a)
     for (int mb = wave; mb < MB; mb += 4) {
         const int64_t m = mb * 16 + lr;
         if (m >= a.m) continue;
-        const int sq = a.sumq[m];
+        const int sq = e_sq;  // mb == wave
         float c0 = 0.0f, c1 = 0.0f;
         if constexpr (EPI != EPI_ACC) {
-            const float s = a.s[m];
-            c0 = token_scale(s, a.gamma0[0], a.qmax);
-            if constexpr (DUAL) c1 = token_scale(s, a.gamma1[0], a.qmax);
+            c0 = token_scale(e_s, g0, a.qmax);
+            if constexpr (DUAL) c1 = token_scale(e_s, g1, a.qmax);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
