@@ -50,6 +50,7 @@ struct BgemvArgs {
     float qmax;
     int rows_per_wg;  // R
     int chunks;       // kp / 64
+    uint32_t g_magic; // ceil(2^32 / (k / 16)): f / G as the high half of f * g_magic (exact for f * G < 2^32)
 };
 
 // RB: 16-row blocks per workgroup (1 or 2). JM: quads per wave. SL: activation
@@ -129,17 +130,15 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     asm volatile("" ::"s"(gam));
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
-        slot_t[s] = slot_f[s] / G;
+        slot_t[s] = (int)__umulhi((uint32_t)slot_f[s], a.g_magic);  // slot_f / G
         slot_g[s] = slot_f[s] - slot_t[s] * G;
     }
 
-    // zero codes: each row's groups G .. GQ, and the rows past the tokens
+    // zero codes of each token's groups G .. GQ (their weight words are real
+    // codes of a clamped chunk). The rows past the tokens are left as they are:
+    // their products land in the columns of tokens the epilogue drops.
     for (int i = tid; i < M * (GQ - G); i += kBT) {
         const int t = i / (GQ - G), g = G + (i - t * (GQ - G));
-        *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
-    }
-    for (int i = tid; i < (16 - M) * GQ; i += kBT) {
-        const int t = M + i / GQ, g = i - (t - M) * GQ;
         *reinterpret_cast<uint4 *>(q_lds + t * QS + g * 16) = make_uint4(0, 0, 0, 0);
     }
 
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(xr[j]));
         const bool valid = tid + s * kBT < NG;
-        const int u0 = f0 / G;
+        const int u0 = (int)__umulhi((uint32_t)f0, a.g_magic);  // f0 / G
         const float m0 = row16_max(valid && slot_t[s] == u0 ? mx : 0.0f);
         const float m1 = row16_max(valid && slot_t[s] != u0 ? mx : 0.0f);
         if (lr == 0) {
@@ -176,7 +175,11 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
     __syncthreads();
 
     // 4. codes into LDS (qperm order) and sum_k q per token (inputs past k
-    //    were zeroed above)
+    //    were zeroed above); the scales of every slot are read first, so the
+    //    slots wait for LDS once
+    float inv_s[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) inv_s[s] = tok_inv[slot_t[s]];
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
         const int f0 = wave * 64 + s * kBT;
@@ -185,10 +188,10 @@ __global__ __launch_bounds__(kBT) void bgemv_kernel(BgemvArgs a)
         int sum = 0;
         if (valid) {
             uint4 pv;
-            sum = quant_group(xk[s], tok_inv[slot_t[s]], &pv, nullptr);
+            sum = quant_group(xk[s], inv_s[s], &pv, nullptr);
             *reinterpret_cast<uint4 *>(q_lds + slot_t[s] * QS + slot_g[s] * 16) = pv;
         }
-        const int u0 = f0 / G;
+        const int u0 = (int)__umulhi((uint32_t)f0, a.g_magic);  // f0 / G
         const int s0 = row16_sum(valid && slot_t[s] == u0 ? sum : 0);
         const int s1 = row16_sum(valid && slot_t[s] != u0 ? sum : 0);
         if (lr == 0) {
@@ -290,6 +293,7 @@ hipError_t launch_bgemv(const GemvProblem &p, hipStream_t st)
     a.w = p.w0; a.ldw = p.ldw; a.gamma = p.gamma0;
     a.out = p.out; a.acc_out = p.acc_out; a.qmax = p.qmax;
     a.chunks = (int)(p.kp / 64);
+    a.g_magic = (uint32_t)ceil_div((int64_t)1 << 32, p.k / 16);
     int64_t r = ceil_div(p.n, (int64_t)256);
     if (r > kBMaxRows) r = kBMaxRows;
     a.rows_per_wg = (int)r;
