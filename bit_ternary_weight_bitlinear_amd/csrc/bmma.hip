@@ -12,8 +12,10 @@
 // get block ids 8 apart, so they land on the same XCD (workgroups go
 // round-robin over the 8 XCDs) at about the same time and share its L2 copy
 // of the tile's weights.
-//  * The 8 waves split the chunk quads (4 x 64 inputs) of k into contiguous
-//    ranges, and each wave works alone until the final reduction: it copies
+//  * The W waves split the chunk quads (4 x 64 inputs) of k into contiguous
+//    ranges (W = 8..12, as many as make the busiest wave's share smallest:
+//    10 waves of one quad for 2560 inputs rather than 8 waves of one or two),
+//    and each wave works alone until the final reduction: it copies
 //    the 16*TB token rows' bytes of its own quads into its own LDS region by
 //    direct global->LDS loads (16 lanes per token and load: 256 contiguous
 //    bytes, whole cache lines), then requests the packed weights of its quads
@@ -36,8 +38,6 @@
 
 namespace bl {
 
-constexpr int kBmT = 512;         // threads per workgroup
-constexpr int kBmW = kBmT / 64;   // waves per workgroup
 constexpr int kBmRegBudget = 64;  // VGPRs for the up-front weight words (NQ * NA * RB * 4)
 constexpr int kBmLdsMax = 160 * 1024 - 1024;  // dynamic LDS (the rest: token scales and sums)
 
@@ -63,16 +63,21 @@ constexpr int bmma_wave_lds(int rb, int tb, int nq, int na)
 {
     return nq * tb * 4096 > na * rb * tb * 1024 ? nq * tb * 4096 : na * rb * tb * 1024;
 }
-// the tiles that fit: the up-front weight words within kBmRegBudget VGPRs, the
-// waves' LDS within the CU's
-constexpr bool bmma_fits(int rb, int tb, int nq, int na)
+// the tiles that fit W waves: the up-front weight words within kBmRegBudget
+// VGPRs, and with the accumulators within what W waves leave each (two waves
+// per SIMD up to W = 8: 256 VGPRs; three: 168, less ~40 for addresses and
+// operands); the waves' LDS within the CU's
+constexpr bool bmma_fits(int rb, int tb, int nq, int na, int w)
 {
-    return nq * na * rb * 4 <= kBmRegBudget && kBmW * bmma_wave_lds(rb, tb, nq, na) <= kBmLdsMax;
+    const int vgprs = w <= 8 ? 256 : 168;
+    return nq * na * rb * 4 <= kBmRegBudget && nq * na * rb * 4 + na * rb * tb * 4 + 40 <= vgprs &&
+           w * bmma_wave_lds(rb, tb, nq, na) <= kBmLdsMax;
 }
 
-template <int RB, int TB, int NQ, int EPI>
-__global__ __launch_bounds__(kBmT) void bmma_kernel(BmmaArgs a)
+template <int RB, int TB, int NQ, int EPI, int W>
+__global__ __launch_bounds__(64 * W) void bmma_kernel(BmmaArgs a)
 {
+    constexpr int kBmW = W, kBmT = 64 * W;  // waves and threads per workgroup
     constexpr bool DUAL = EPI == EPI_GATE;
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int WL = bmma_wave_lds(RB, TB, NQ, NA);
@@ -251,91 +256,121 @@ __global__ __launch_bounds__(kBmT) void bmma_kernel(BmmaArgs a)
 namespace {
 
 struct BmmaShape {
-    int rb = 0, tb = 0, ts = 0, nq = 0;
+    int rb = 0, tb = 0, ts = 0, nq = 0, w = 0;
 };
 
-// quads per wave: ceil(C / 32). At most 4 fit (8 waves x 4 quads x 16 tokens x
-// 256 bytes of LDS), i.e. rows of up to 8192 inputs; longer ones go to the
-// skinny kernel.
-int64_t bmma_nq(int64_t C) { return ceil_div(C, (int64_t)(4 * kBmW)); }
+// quads per wave with w waves: ceil(ceil(C / 4) / w). With 8 waves at most 4
+// fit (8 waves x 4 quads x 16 tokens x 256 bytes of LDS), i.e. rows of up to
+// 8192 inputs; longer ones go to the skinny kernel.
+int64_t bmma_nq(int64_t C, int w = 8) { return ceil_div(ceil_div(C, (int64_t)4), (int64_t)w); }
+
+// Waves per workgroup: the count among 8, 9, 10 and 12 that gives the busiest
+// wave the fewest quads (the fewest waves among equals), as long as the
+// smallest tile fits. The workgroup's bytes do not change with it; what does
+// is how long its slowest wave runs: with 2560 inputs (10 quads) 8 waves
+// leave two waves with two quads while the others wait for them at the final
+// barrier. (16 waves of two quads for 6912 inputs measured slower than 9 of
+// three: 25.7 against 25.5 us for a 2B layer at 8 tokens.)
+int bmma_waves(int64_t C, int na)
+{
+    int best = 8;
+    for (int w : {9, 10, 12})
+        if (bmma_nq(C, w) < bmma_nq(C, best) && bmma_fits(1, 1, (int)bmma_nq(C, w), na, w)) best = w;
+    return best;
+}
 
 // The tile for m tokens, n rows, kp inputs: among RB in {1, 2, 4} and TB in
 // 1..4 (TS = ceil(m / 16 TB) token slices), the one whose busiest CU takes
 // the least time: its token rows from L2 at about 67 GB/s and its weights
 // from HBM at about 26 GB/s (what one CU keeps in flight over each latency),
 // workgroups beyond the 256 CUs in further rounds, with the MFMA issue time
-// (16 cycles per step, two waves per SIMD, 2.4 GHz) as the floor.
+// (16 cycles per step, W / 4 waves per SIMD, 2.4 GHz) as the floor.
 BmmaShape bmma_shape(int64_t m, int64_t n, int64_t kp, bool dual)
 {
     const int na = dual ? 2 : 1;
-    const int64_t C = kp / 64, nq = bmma_nq(C);
+    const int64_t C = kp / 64;
+    const int w = bmma_waves(C, na);
+    const int64_t nq = bmma_nq(C, w);
     BmmaShape best;
     double best_cost = 0.0;
     for (int rb = 1; rb <= 4; rb *= 2) {
         for (int tb = 1; tb <= 4; ++tb) {
-            if (!bmma_fits(rb, tb, (int)nq, na)) continue;
+            if (!bmma_fits(rb, tb, (int)nq, na, w)) continue;
             const int64_t ts = ceil_div(m, (int64_t)(16 * tb));
             const int64_t tiles = ceil_div(n, (int64_t)(16 * rb));
             const int64_t rounds = ceil_div(tiles * ts, (int64_t)256);
             const double mem_ns = 16.0 * tb * kp / 67.0 + 4.0 * rb * na * kp / 26.0;
-            const double mfma_ns = (double)nq * 4 * na * rb * tb * 16.0 * 2.0 / 2.4;
+            const double mfma_ns = (double)nq * 4 * na * rb * tb * 16.0 * (w / 4.0) / 2.4;
             const double cost = (double)rounds * (mem_ns > mfma_ns ? mem_ns : mfma_ns);
             if (best.rb == 0 || cost < best_cost) {
                 best_cost = cost;
-                best.rb = rb; best.tb = tb; best.ts = (int)ts; best.nq = (int)nq;
+                best.rb = rb; best.tb = tb; best.ts = (int)ts; best.nq = (int)nq; best.w = w;
             }
         }
     }
     return best;
 }
 
-template <int RB, int TB, int NQ, int EPI>
+template <int RB, int TB, int NQ, int EPI, int W>
 hipError_t bm_launch(const BmmaArgs &a, dim3 grid, hipStream_t st)
 {
     constexpr int NA = EPI == EPI_GATE ? 2 : 1;
-    if constexpr (bmma_fits(RB, TB, NQ, NA)) {
-        const int lds = kBmW * bmma_wave_lds(RB, TB, NQ, NA);
-        const auto kern = bmma_kernel<RB, TB, NQ, EPI>;
+    if constexpr (bmma_fits(RB, TB, NQ, NA, W)) {
+        const int lds = W * bmma_wave_lds(RB, TB, NQ, NA);
+        const auto kern = bmma_kernel<RB, TB, NQ, EPI, W>;
         static LdsLimit lim;
         if (hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds, lim)) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(kBmT), (size_t)lds, st, a);
+        hipLaunchKernelGGL(kern, grid, dim3(64 * W), (size_t)lds, st, a);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
     }
 }
 
-template <int RB, int TB, int NQ>
+template <int RB, int TB, int NQ, int W>
 hipError_t bm_epi(const BmmaArgs &a, int epi, dim3 grid, hipStream_t st)
 {
     switch (epi) {
-    case EPI_Y: return bm_launch<RB, TB, NQ, EPI_Y>(a, grid, st);
-    case EPI_ACC: return bm_launch<RB, TB, NQ, EPI_ACC>(a, grid, st);
-    default: return bm_launch<RB, TB, NQ, EPI_GATE>(a, grid, st);
+    case EPI_Y: return bm_launch<RB, TB, NQ, EPI_Y, W>(a, grid, st);
+    case EPI_ACC: return bm_launch<RB, TB, NQ, EPI_ACC, W>(a, grid, st);
+    default: return bm_launch<RB, TB, NQ, EPI_GATE, W>(a, grid, st);
     }
 }
 
-template <int RB, int TB>
+// quads per wave: at most ceil(32 / W) (rows of up to 8192 inputs)
+template <int RB, int TB, int W>
 hipError_t bm_nq(int nq, const BmmaArgs &a, int epi, dim3 grid, hipStream_t st)
 {
     switch (nq) {
-    case 1: return bm_epi<RB, TB, 1>(a, epi, grid, st);
-    case 2: return bm_epi<RB, TB, 2>(a, epi, grid, st);
-    case 3: return bm_epi<RB, TB, 3>(a, epi, grid, st);
-    case 4: return bm_epi<RB, TB, 4>(a, epi, grid, st);
+    case 1: return bm_epi<RB, TB, 1, W>(a, epi, grid, st);
+    case 2: return bm_epi<RB, TB, 2, W>(a, epi, grid, st);
+    case 3: return bm_epi<RB, TB, 3, W>(a, epi, grid, st);
+    case 4:
+        if constexpr (W <= 10) return bm_epi<RB, TB, 4, W>(a, epi, grid, st);
+        else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int RB>
+template <int RB, int W>
 hipError_t bm_tb(int tb, int nq, const BmmaArgs &a, int epi, dim3 grid, hipStream_t st)
 {
     switch (tb) {
-    case 1: return bm_nq<RB, 1>(nq, a, epi, grid, st);
-    case 2: return bm_nq<RB, 2>(nq, a, epi, grid, st);
-    case 3: return bm_nq<RB, 3>(nq, a, epi, grid, st);
-    case 4: return bm_nq<RB, 4>(nq, a, epi, grid, st);
+    case 1: return bm_nq<RB, 1, W>(nq, a, epi, grid, st);
+    case 2: return bm_nq<RB, 2, W>(nq, a, epi, grid, st);
+    case 3: return bm_nq<RB, 3, W>(nq, a, epi, grid, st);
+    case 4: return bm_nq<RB, 4, W>(nq, a, epi, grid, st);
     default: return hipErrorInvalidValue;
+    }
+}
+
+template <int W>
+hipError_t bm_rb(const BmmaShape &sh, const BmmaArgs &a, int epi, dim3 grid, hipStream_t st)
+{
+    switch (sh.rb) {
+    case 1: return bm_tb<1, W>(sh.tb, sh.nq, a, epi, grid, st);
+    case 2: return bm_tb<2, W>(sh.tb, sh.nq, a, epi, grid, st);
+    default: return bm_tb<4, W>(sh.tb, sh.nq, a, epi, grid, st);
     }
 }
 
@@ -345,7 +380,7 @@ bool bmma_supported(int64_t m, int64_t kp, bool dual)
 {
     if (m < 1 || m > 64 || kp < 64) return false;
     const int64_t nq = bmma_nq(kp / 64);
-    return nq <= 4 && bmma_fits(1, 1, (int)nq, dual ? 2 : 1);
+    return nq <= 4 && bmma_fits(1, 1, (int)nq, dual ? 2 : 1, 8);
 }
 
 hipError_t launch_bmma(const GemmProblem &p, hipStream_t st)
@@ -362,10 +397,11 @@ hipError_t launch_bmma(const GemmProblem &p, hipStream_t st)
     a.ts = sh.ts;
     a.row_tiles = (int)ceil_div(p.n, (int64_t)(16 * sh.rb));
     const dim3 grid((unsigned)(ceil_div((int64_t)a.row_tiles, (int64_t)8) * 8 * sh.ts));
-    switch (sh.rb) {
-    case 1: return bm_tb<1>(sh.tb, sh.nq, a, p.epi, grid, st);
-    case 2: return bm_tb<2>(sh.tb, sh.nq, a, p.epi, grid, st);
-    default: return bm_tb<4>(sh.tb, sh.nq, a, p.epi, grid, st);
+    switch (sh.w) {
+    case 8: return bm_rb<8>(sh, a, p.epi, grid, st);
+    case 9: return bm_rb<9>(sh, a, p.epi, grid, st);
+    case 10: return bm_rb<10>(sh, a, p.epi, grid, st);
+    default: return bm_rb<12>(sh, a, p.epi, grid, st);
     }
 }
 
