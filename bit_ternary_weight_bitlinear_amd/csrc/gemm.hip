@@ -54,6 +54,7 @@ struct GemmArgs {
     const float *gamma0, *gamma1;
     float *out;
     int32_t *acc_out;
+    int64_t ldo;  // row stride of out / acc_out (>= n: a column range of a wider output)
     float qmax;
     int n_tiles, m_tiles;
 };
@@ -90,7 +91,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
     constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
     float *const out = a.out;
     int32_t *const acc_out = a.acc_out;
-    const int64_t M = a.m, N = a.n;
+    const int64_t M = a.m, N = a.n, LDO = a.ldo;
     float g0 = 0.0f, g1 = 0.0f;
     if constexpr (EPI != EPI_ACC) {
         g0 = a.gamma0[0];
@@ -119,7 +120,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
                 for (int e = 0; e < 4; ++e) {
                     const int64_t m = m0 + r + e;
                     if (!FULL && m >= M) continue;
-                    const int64_t row = m * N + n0 + lrow;
+                    const int64_t row = m * LDO + n0 + lrow;
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn) {
                         if (!FULL && n0 + fn * 32 + lrow >= N) continue;
@@ -446,28 +447,44 @@ static hipError_t launch_fm1(const GemmArgs &a, hipStream_t st)
 // all 256 AGPRs and 256 VGPRs).
 struct TileShape {
     int fm, fn;
+    double cost;  // modelled time: rounds over the 256 CUs x per-tile cost
 };
 static bool tile_allowed(int fm, int fn, int na)
 {
     if (na == 2) return (fm == 1 && fn <= 6) || (fm == 2 && fn == 4);
     return fm * fn <= 14;
 }
+static int64_t tile_count(int64_t m, int64_t n, int fm, int fn) { return ceil_div(n, 32 * fn) * ceil_div(m, 128 * fm); }
 static TileShape pick_tile(int64_t m, int64_t n, int na)
 {
-    TileShape best{1, 4};
-    double best_cost = 1e300;
+    TileShape best{1, 4, 1e300};
     for (int fm = 2; fm >= 1; --fm)
         for (int fn = 8; fn >= 4; --fn) {
             if (!tile_allowed(fm, fn, na)) continue;
-            const int64_t tiles = ceil_div(n, 32 * fn) * ceil_div(m, 128 * fm);
-            const int64_t rounds = ceil_div(tiles, 256);
+            const int64_t rounds = ceil_div(tile_count(m, n, fm, fn), 256);
             const double cost = (double)rounds * (fm * fn * na * (1.0 + 0.2 / fm) + 3.0);
-            if (cost < best_cost) {
-                best_cost = cost;
-                best = TileShape{fm, fn};
-            }
+            if (cost < best.cost) best = TileShape{fm, fn, cost};
         }
     return best;
+}
+
+// Output columns given to a second launch. When the best tiling leaves its last
+// round over the 256 CUs at most half full (the 8B gate/up pair at 2048 tokens:
+// 896 tiles of 256x128, 3.5 rounds), the columns of the full rounds keep that
+// tiling and the rest run as a launch of their own, whose smaller tiles spread
+// over all CUs (there: 12288 + 2048 columns, the latter as 256 tiles of 128x128).
+// Returns the column count of the first launch, or n for one launch. The
+// modelled cost adds one block-cost unit per extra launch.
+static int64_t split_columns(int64_t m, int64_t n, int na)
+{
+    const TileShape t = pick_tile(m, n, na);
+    const int64_t tiles = tile_count(m, n, t.fm, t.fn), last = tiles % 256;
+    if (tiles <= 256 || last == 0 || last > 128) return n;
+    const int64_t m_tiles = ceil_div(m, 128 * t.fm);
+    const int64_t n_main = (tiles / 256) * 256 / m_tiles * (32 * t.fn);
+    if (n_main <= 0 || n_main >= n) return n;
+    const double split = pick_tile(m, n_main, na).cost + pick_tile(m, n - n_main, na).cost + 1.0;
+    return split < t.cost ? n_main : n;
 }
 
 template <int EPI>
@@ -506,13 +523,28 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t st)
     GemmArgs a;
     a.qp = p.qp; a.kp = p.kp; a.s = p.s; a.sumq = p.sumq; a.m = p.m; a.n = p.n;
     a.w0 = p.w0; a.w1 = p.w1; a.ldw = p.ldw; a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
-    a.out = p.out; a.acc_out = p.acc_out; a.qmax = p.qmax;
+    a.out = p.out; a.acc_out = p.acc_out; a.ldo = p.n; a.qmax = p.qmax;
     a.n_tiles = a.m_tiles = 0;
-    switch (p.epi) {
-    case EPI_Y: return launch_epi<EPI_Y>(a, st);
-    case EPI_ACC: return launch_epi<EPI_ACC>(a, st);
-    default: return launch_epi<EPI_GATE>(a, st);
-    }
+    auto run = [&](const GemmArgs &g) {
+        switch (p.epi) {
+        case EPI_Y: return launch_epi<EPI_Y>(g, st);
+        case EPI_ACC: return launch_epi<EPI_ACC>(g, st);
+        default: return launch_epi<EPI_GATE>(g, st);
+        }
+    };
+    const int64_t n_main = split_columns(p.m, p.n, p.epi == EPI_GATE ? 2 : 1);
+    if (n_main == p.n) return run(a);
+    // columns [0, n_main) and [n_main, n): weight rows and output columns offset,
+    // output row stride unchanged
+    GemmArgs b = a;
+    a.n = n_main;
+    b.n = p.n - n_main;
+    b.w0 = p.w0 + n_main * p.ldw;
+    if (p.w1) b.w1 = p.w1 + n_main * p.ldw;
+    if (p.out) b.out = p.out + n_main;
+    if (p.acc_out) b.acc_out = p.acc_out + n_main;
+    if (hipError_t e = run(a)) return e;
+    return run(b);
 }
 
 }  // namespace bl

@@ -176,6 +176,31 @@ def test_gemm_i32_bmma_tiles(bl, m, k, n):
     np.testing.assert_array_equal(host(acc), q.astype(np.int64) @ wt.astype(np.int64).T)
 
 
+# Shapes whose best GEMM tiling would leave its last round over the 256 CUs at
+# most half full: the columns of the full rounds run as one launch and the rest
+# as a second one with smaller tiles, writing into the same output rows.
+# 2561 x 15488: 1063 tiles of 256x192, split at column 13248; 1153 x 34304:
+# 1080 tiles, split at 29376 (the tail on 128-token tiles).
+@pytest.mark.parametrize("m,k,n", [(2561, 256, 15488), (1153, 192, 34304)])
+def test_forward_gemm_column_split(bl, m, k, n):
+    w, p_ref, g_ref, _ = make_linear(97, 1, n, k)
+    x = synth.activations(97, m, k, dtype="bf16", outlier_channels=2, outlier_scale=20.0)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward(to_dev(x, "bf16"), packed, gamma, return_acc=True)
+    r = oracle.forward(x, p_ref, g_ref, k, "bf16")
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
+
+
+def test_gemm_i32_column_split(bl):
+    m, k, n = 2561, 128, 15488
+    rng = np.random.default_rng(11)
+    q = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    w, p_ref, _, wt = make_linear(98, 1, n, k)
+    acc = bl.gemm_i32(to_dev(q), to_dev(p_ref))
+    np.testing.assert_array_equal(host(acc), q.astype(np.int64) @ wt.astype(np.int64).T)
+
+
 # the largest sizes the boundary accepts (BL_MAX_DIM = 2^20 inputs or outputs,
 # BL_MAX_TOKENS = 2^22 tokens), each with the other dimensions small
 MAX_SHAPES = [(2, 1 << 20, 5), (1, 20, 1 << 20), (1 << 22, 4, 3)]
@@ -290,7 +315,8 @@ def _ffn_case(bl, cfg, m, hid, f, dtype="bf16"):
 @pytest.mark.parametrize("m,hid,f", [(1, 256, 512), (3, 260, 516), (4, 512, 1024), (5, 256, 512),
                                      (33, 260, 516), (130, 512, 768),
                                      (1, 256, 20000),  # gate/up pair with more than 64 rows per workgroup
-                                     (2, 8, 1 << 20)])  # the largest ffn width the boundary accepts
+                                     (2, 8, 1 << 20),  # the largest ffn width the boundary accepts
+                                     (300, 256, 33024)])  # gate/up pair as two launches (columns split at 27200)
 def test_ffn_small(bl, m, hid, f):
     _ffn_case(bl, 96, m, hid, f)
 
