@@ -23,6 +23,9 @@ so whatever --steps is, each timed step reads its weights from HBM.
 Timing: steps are captured in HIP graphs (no host launch overhead) and timed
 with HIP events on the stream the library launches on (torch's current
 stream). The headline times exactly --steps steps after --warmup eager ones.
+Before every timed region the region's own graph is also replayed untimed for
+0.25 s: this GPU raises its clocks over the first ~0.1 s of sustained load, and
+compute-bound workloads run ~10 % slower in a region started from idle.
 `roofline` is for the dominant kernel of the headline, the decode GEMV: its
 average launch duration comes from graphs of that kernel alone over the pool
 (events, this run); the figure from the committed rocprofv3 kernel trace is
@@ -89,7 +92,15 @@ def r4(v):
 class Timer:
     """Times graph replays with HIP events on torch's current stream (the stream
     the library launches on). `flush` streams 1 GiB of unrelated memory through
-    the caches before each timed region."""
+    the caches before each timed region.
+
+    Before each timed region the workload's own graph is replayed untimed for
+    at least WARM_S seconds: this GPU raises its clocks over the first ~0.1 s of
+    sustained load (the 8B FFN at 2048 tokens takes ~408 us per call in a region
+    started from idle and ~370 us from 0.1 s of load on), so a region started
+    cold measures the clock ramp, not the kernels."""
+
+    WARM_S = 0.25
 
     def __init__(self, torch, dev):
         self.torch = torch
@@ -113,6 +124,16 @@ class Timer:
         t.cuda.synchronize()
         return g
 
+    def warm(self, graphs):
+        """Replays the graphs untimed until WARM_S seconds have passed (at least once)."""
+        t0 = time.perf_counter()
+        while True:
+            for g in graphs:
+                g.replay()
+            self.torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= self.WARM_S:
+                return
+
     def _events(self, body):
         t = self.torch
         st = t.cuda.current_stream()
@@ -125,15 +146,13 @@ class Timer:
 
     def steps_region(self, fn, steps, cycle):
         """Exactly `steps` steps: a graph of one pool cycle replayed steps // cycle
-        times, then a graph of the remaining steps. Each graph is replayed once
-        untimed, then the caches are flushed. Returns seconds per step."""
+        times, then a graph of the remaining steps. The graphs are replayed untimed
+        for WARM_S seconds, then the caches are flushed. Returns seconds per step."""
         steps = max(1, steps)
         reps, rest = divmod(steps, cycle)
         g = self.capture(fn, cycle) if reps else None
         g_rest = self.capture(fn, rest) if rest else None
-        for gr in (g, g_rest):
-            if gr is not None:
-                gr.replay()
+        self.warm([gr for gr in (g, g_rest) if gr is not None])
         self.flush()
 
         def body():
@@ -145,10 +164,10 @@ class Timer:
 
     def launch_mean(self, fn, cycle, seconds=0.3):
         """Mean time per call of `fn` from a graph of `cycle` calls (one pool
-        cycle) replayed for about `seconds`, after an untimed replay and a flush."""
+        cycle) replayed for about `seconds`, after WARM_S seconds of untimed
+        replays and a flush."""
         g = self.capture(fn, cycle)
-        g.replay()
-        self.torch.cuda.synchronize()
+        self.warm([g])
         t0 = time.perf_counter()
         g.replay()
         self.torch.cuda.synchronize()
@@ -794,7 +813,8 @@ def main():
         "config": {"workload": "decode GEMV m=1: 2B-class FFN up 2560->6912 + down 6912->2560, bf16 "
                                "activations (1% channels x30), packed weights cold from HBM",
                    "m": 1, "shapes_k_n": dec["shapes"], "packed_bytes_per_step": dec["packed_bytes_per_step"],
-                   "rotation_pool_bytes": dec["pool_bytes"], "cache_flush_bytes_before_timing": 2 * FLUSH_BYTES},
+                   "rotation_pool_bytes": dec["pool_bytes"], "cache_flush_bytes_before_timing": 2 * FLUSH_BYTES,
+                   "untimed_replay_s_before_timing": Timer.WARM_S},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,
