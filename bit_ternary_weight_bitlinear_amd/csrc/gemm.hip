@@ -3,9 +3,13 @@
 // At many tokens the W1.58A8 product ("穿越1比特的奇幻旅程", section 推理实现 / GPU端)
 // is a dense contraction, so it runs on v_mfma_i32_32x32x32_i8 with the
 // activations as operand A and the ternary codes as operand B:
-//  * a workgroup (4 waves) owns a tile of 128*FM tokens x 32*FN output
-//    features; wave w takes tokens [32*FM*w, 32*FM*(w+1)) of it against all
-//    32*FN features (FM*FN accumulator blocks of 32x32);
+//  * a workgroup owns a tile of 128*FM tokens x 32*FN output features. With
+//    four waves, wave w takes tokens [32*FM*w, 32*FM*(w+1)) of it against all
+//    32*FN features (FM*FN accumulator blocks of 32x32). 256-token tiles run
+//    eight waves, two per SIMD: waves w and w+4 take the same tokens, one the
+//    first (FN+1)/2 feature fragments and the other the rest, so while one
+//    waits at a barrier or for LDS the other keeps the SIMD's matrix core busy
+//    (same MFMA work per SIMD, half the accumulators per wave);
 //  * two LDS rings, filled by direct global->LDS loads (global_load_lds_dwordx4)
 //    issued DB k-steps ahead: the qperm activation tile of each 64-input step
 //    (64-byte rows) and the packed weight rows of that step (16-byte rows).
@@ -77,18 +81,20 @@ __device__ inline uint64_t shr64(uint64_t v)
 // Epilogue of one wave (y goes out with non-temporal stores; h of a gate/up
 // pair with plain ones, since the requantization reads it right after and
 // finds part of it in the caches: 22.3 against 26.5 us at 2048 x 14336):
-// y = (float)(acc - sumq) * ((s / 127) * gamma) for its
-// 32*FM tokens (tile rows wave*32*FM ..) x 32*FN features. tok_sq / tok_s hold
-// sum_k q and s of the tile's tokens (LDS). Interior tiles store without bounds
-// checks, one row pointer per token and immediate offsets per block.
-template <int FM, int FN, int EPI>
+// y = (float)(acc - sumq) * ((s / 127) * gamma) for its 32*FM tokens (tile
+// rows tokw*32*FM ..) x its FN fragments of 32 features, starting at tile
+// column 32*FOFF. tok_sq / tok_s hold sum_k q and s of the tile's tokens
+// (LDS). Interior tiles store without bounds checks, one row pointer per token
+// and immediate offsets per block.
+template <int FM, int FN, int FOFF, int EPI>
 __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[EPI == EPI_GATE ? 2 : 1][FM][FN],
-                                           const int *tok_sq, const float *tok_s, int64_t m0, int64_t n0,
-                                           int wave, int lrow, int lhalf)
+                                           const int *tok_sq, const float *tok_s, int64_t m0, int64_t n0t,
+                                           int tokw, int lrow, int lhalf)
 {
     constexpr bool DUAL = EPI == EPI_GATE;
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
+    const int64_t n0 = n0t + 32 * FOFF;
     float *const out = a.out;
     int32_t *const acc_out = a.acc_out;
     const int64_t M = a.m, N = a.n, LDO = a.ldo;
@@ -104,7 +110,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = wave * WM + fm * 32 + 8 * j + 4 * lhalf;  // tile row of register 4j
+                const int r = tokw * WM + fm * 32 + 8 * j + 4 * lhalf;  // tile row of register 4j
                 const v4i sq = *reinterpret_cast<const v4i *>(tok_sq + r);
                 float c0e[4] = {0.0f, 0.0f, 0.0f, 0.0f}, c1e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (EPI != EPI_ACC) {
@@ -157,16 +163,25 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
     }
 }
 
-// SPB: 64-input steps per ring stage (1 or 2). With 2, the direct loads of a
-// stage go out once per pair of steps and the barrier runs once per pair; the
-// step count must be even. DB: stages requested ahead.
-template <int FM, int FN, int EPI, int DB, int SPB>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+// The work of one wave of a tile of 128*FM tokens x 32*FN features, run by NW
+// waves: wave w takes tokens [32*FM*(w%4), 32*FM*(w%4+1)) of the tile against
+// its FW fragments of 32 features starting at fragment FOFF. With NW = 4 every
+// wave has all FN fragments; with NW = 8 (two waves per SIMD) waves 0-3 take
+// the first (FN+1)/2 fragments and waves 4-7 the rest, so each SIMD keeps the
+// same MFMA work with half the accumulators per wave, and one wave's barrier
+// and LDS waits can be covered by the other's MFMAs. The direct loads of a
+// step are spread over all NW waves (the packed weight rows over waves 0-3:
+// WLOAD). SPB: 64-input steps per ring stage (1 or 2). With 2, the direct
+// loads of a stage go out once per pair of steps and the barrier runs once per
+// pair; the step count must be even. DB: stages requested ahead.
+template <int FM, int FN, int EPI, int DB, int SPB, int NW, int FW, int FOFF, bool WLOAD>
+__device__ __forceinline__ void gemm_waves(const GemmArgs &a, int8_t *smem, int wave, int64_t m0, int64_t n0)
 {
     constexpr bool DUAL = EPI == EPI_GATE;
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
-    static_assert(FM * FN * NA <= 16, "accumulators fit the 256 AGPRs");
+    static_assert(FM * FW * NA <= 16, "accumulators fit the 256 AGPRs");
+    static_assert(NW == 4 || (NW == 8 && FM * FW * NA <= 8), "two waves per SIMD: half the accumulators");
     static_assert(BN <= 256, "packed rows: one 64-row direct load per wave");
     static_assert(DB >= 3, "at least one stage of slack for the direct loads");
     static_assert(SPB == 1 || SPB == 2, "one or two steps per stage");
@@ -179,33 +194,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     // during its first step).
     constexpr int SBX = DB + 1;
     constexpr int SBW = SPB == 1 ? DB : DB + 1;
-    constexpr int X_INSTR = BM / 64;       // activation direct loads per thread per step
-    constexpr int DPS = SPB * (X_INSTR + NA);  // direct loads per thread per stage
+    constexpr int X_INSTR = BM / (16 * NW);  // activation direct loads per thread per step
+    static_assert(X_INSTR * 16 * NW == BM, "activation rows split evenly over the waves");
+    constexpr int DPS = SPB * (X_INSTR + (WLOAD ? NA : 0));  // direct loads per thread per stage
     constexpr int VM_SLACK = (DB - 2) * DPS;
     static_assert(VM_SLACK < 64, "vmcnt field");
     // LDS: xring[SBX][XS], wring[SBW][WS], then sum_k q and s of the tile's tokens
     constexpr int XR = 0, WR = SBX * XS, TQ = WR + SBW * WS, TS = TQ + BM * 4;
-    extern __shared__ __align__(16) int8_t smem[];
     const uint32_t lds0 = lds_addr(smem);
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int tokw = wave & 3;  // token group of the tile
     const int lrow = lane & 31, lhalf = lane >> 5;
 
-    // XCD-aware tile order: workgroups id, id+8, id+16, ... share an XCD and get
-    // consecutive tiles, row-major over (m tile, n tile)
-    const int tiles = a.n_tiles * a.m_tiles;
-    const int id = blockIdx.x, xcd = id & 7, per = tiles >> 3, rem = tiles & 7;
-    const int tile = xcd * per + min(xcd, rem) + (id >> 3);
-    const int64_t m0 = (int64_t)(tile / a.n_tiles) * BM, n0 = (int64_t)(tile % a.n_tiles) * BN;
     const int nks = (int)(a.kp / 64);
-
     // direct-load sources: scalar bases advanced per step, constant per-lane offsets
     const int8_t *xbase = a.qp + m0 * a.kp;
     uint32_t xoff[X_INSTR];
 #pragma unroll
     for (int i = 0; i < X_INSTR; ++i) {
-        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+        const int row = (i * NW + wave) * 16 + (lane >> 2);
         const int g = (lane & 3) ^ ((row >> 2) & 3);
         xoff[i] = (uint32_t)(row * a.kp + g * 16);
     }
@@ -226,38 +234,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             const int64_t ks = (int64_t)SPB * j + sub;
 #pragma unroll
             for (int i = 0; i < X_INSTR; ++i)
-                dma16(xbase + ks * 64, xoff[i], lds0 + XR + xo + sub * X_TILE + (i * 4 + wave) * 1024);
+                dma16(xbase + ks * 64, xoff[i], lds0 + XR + xo + sub * X_TILE + (i * NW + wave) * 1024);
+            if constexpr (WLOAD) {
 #pragma unroll
-            for (int mat = 0; mat < NA; ++mat)
-                dma16(wbase[mat] + ks * 16, woff, lds0 + WR + wo + sub * W_STAGE + mat * W_PK + wave * 1024);
+                for (int mat = 0; mat < NA; ++mat)
+                    dma16(wbase[mat] + ks * 16, woff, lds0 + WR + wo + sub * W_STAGE + mat * W_PK + wave * 1024);
+            }
         }
     };
 
     // LDS read addresses: per-lane bases, stage offsets added per step
-    const uint32_t xl0 = XR + tile_off(wave * WM + lrow, 2 * lhalf);      // half 0: group 2*lhalf
-    const uint32_t xl1 = XR + tile_off(wave * WM + lrow, 1 + 2 * lhalf);  // half 1: group 1 + 2*lhalf
+    const uint32_t xl0 = XR + tile_off(tokw * WM + lrow, 2 * lhalf);      // half 0: group 2*lhalf
+    const uint32_t xl1 = XR + tile_off(tokw * WM + lrow, 1 + 2 * lhalf);  // half 1: group 1 + 2*lhalf
     const uint32_t wl = WR + lrow * 16 + lhalf * 8;
     // fragments fm sit 32 rows (2 KB) apart with the same swizzle: (row >> 2) & 3 depends on row % 16 only
     auto read_x = [&](uint32_t addr, v4i (&x)[FM]) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) x[fm] = *reinterpret_cast<const v4i *>(smem + addr + fm * 2048);
     };
-    // packed weights of a step: dwords 2*lhalf and 2*lhalf+1 of each of the tile's rows
-    auto read_w = [&](uint32_t addr, v2u (&w)[NA][FN]) {
+    // packed weights of a step: dwords 2*lhalf and 2*lhalf+1 of each of the wave's rows
+    auto read_w = [&](uint32_t addr, v2u (&w)[NA][FW]) {
 #pragma unroll
         for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                w[mat][fn] = *reinterpret_cast<const v2u *>(smem + addr + mat * W_PK + fn * 512);
+            for (int fn = 0; fn < FW; ++fn)
+                w[mat][fn] = *reinterpret_cast<const v2u *>(smem + addr + mat * W_PK + (FOFF + fn) * 512);
     };
 
-    v16i acc[NA][FM][FN];
+    v16i acc[NA][FM][FW];
 #pragma unroll
     for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FW; ++fn)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mat][fm][fn][v] = 0;
 
@@ -275,11 +285,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     // first half step: expands every fragment but the first (whose operands
     // were prepared before the barrier), keeping the second half's operands,
     // and runs the MFMAs of the first half as soon as each is ready
-    auto mfma_half0_rest = [&](const v4i (&x)[FM], const v2u (&w)[NA][FN], v4i (&b1)[NA][FN]) {
+    auto mfma_half0_rest = [&](const v4i (&x)[FM], const v2u (&w)[NA][FW], v4i (&b1)[NA][FW]) {
 #pragma unroll
         for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
+            for (int fn = 0; fn < FW; ++fn) {
                 if (mat == 0 && fn == 0) continue;
                 v4i b0;
                 expand2(w[mat][fn], b0, b1[mat][fn]);
@@ -288,11 +298,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                     acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b0, acc[mat][fm][fn], 0, 0, 0);
             }
     };
-    auto mfma_half1 = [&](const v4i (&x)[FM], const v4i (&b1)[NA][FN]) {
+    auto mfma_half1 = [&](const v4i (&x)[FM], const v4i (&b1)[NA][FW]) {
 #pragma unroll
         for (int mat = 0; mat < NA; ++mat)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FW; ++fn)
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
                     acc[mat][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[fm], b1[mat][fn], acc[mat][fm][fn], 0, 0, 0);
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         o = o >= end ? o - end : o;
     };
 
-    v2u wA[NA][FN], wB[NA][FN];
+    v2u wA[NA][FW], wB[NA][FW];
     v4i x[FM];
     read_w(wl, wA);
     read_x(xl0, x);
@@ -333,8 +343,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     // last. The reads of the next step's data run unconditionally (straight-line
     // code keeps the compiler's LDS wait counts exact); in the last step they
     // read stages that are never used.
-    auto step = [&](v2u (&wc)[NA][FN], v2u (&wn)[NA][FN], uint32_t ya, uint32_t wa, uint32_t xa, auto &&issue) {
-        v4i b1[NA][FN];
+    auto step = [&](v2u (&wc)[NA][FW], v2u (&wn)[NA][FW], uint32_t ya, uint32_t wa, uint32_t xa, auto &&issue) {
+        v4i b1[NA][FW];
         b1[0][0] = p1;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         // registers alternate without copies; no branch inside the body (a merge
         // of the accumulators there costs register-class copies), the odd last
         // step runs after the loop
-        auto one = [&](int ks, v2u (&wc)[NA][FN], v2u (&wn)[NA][FN]) {
+        auto one = [&](int ks, v2u (&wc)[NA][FW], v2u (&wn)[NA][FW]) {
             const bool issue = ks + DB < nks;
             step(wc, wn, xl1 + xs_cur, wl + ws_nxt, xl0 + xs_nxt, [&] {
                 if (issue) dma_stage(ks + DB, xs_iss, ws_iss);
@@ -408,11 +418,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
 
     // epilogue (the loop's last barrier made the per-token terms visible)
-    store_tile<FM, FN, EPI>(a, acc, reinterpret_cast<const int *>(smem + TQ), reinterpret_cast<const float *>(smem + TS),
-                            m0, n0, wave, lrow, lhalf);
+    store_tile<FM, FW, FOFF, EPI>(a, acc, reinterpret_cast<const int *>(smem + TQ),
+                                  reinterpret_cast<const float *>(smem + TS), m0, n0, tokw, lrow, lhalf);
 }
 
-template <int FM, int FN, int EPI, int DB, int SPB = 1>
+// WSPLIT = 1: four waves, each with all FN fragments; 2: eight waves, two per
+// SIMD, splitting the fragments (gemm_waves)
+template <int FM, int FN, int EPI, int DB, int SPB, int WSPLIT>
+__global__ __launch_bounds__(256 * WSPLIT) void gemm_kernel(GemmArgs a)
+{
+    constexpr int BM = 128 * FM, BN = 32 * FN;
+    extern __shared__ __align__(16) int8_t smem[];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // XCD-aware tile order: workgroups id, id+8, id+16, ... share an XCD and get
+    // consecutive tiles, row-major over (m tile, n tile)
+    const int tiles = a.n_tiles * a.m_tiles;
+    const int id = blockIdx.x, xcd = id & 7, per = tiles >> 3, rem = tiles & 7;
+    const int tile = xcd * per + min(xcd, rem) + (id >> 3);
+    const int64_t m0 = (int64_t)(tile / a.n_tiles) * BM, n0 = (int64_t)(tile % a.n_tiles) * BN;
+    const int nks = (int)(a.kp / 64);
+
+    if constexpr (WSPLIT == 1) {
+        gemm_waves<FM, FN, EPI, DB, SPB, 4, FN, 0, true>(a, smem, wave, m0, n0);
+    } else {
+        constexpr int F0 = (FN + 1) / 2;
+        if (wave < 4) gemm_waves<FM, FN, EPI, DB, SPB, 8, F0, 0, true>(a, smem, wave, m0, n0);
+        else gemm_waves<FM, FN, EPI, DB, SPB, 8, FN - F0, F0, false>(a, smem, wave, m0, n0);
+    }
+}
+
+// 256-token tiles run with eight waves (two per SIMD, the fragments split)
+template <int FM, int FN, int EPI, int DB, int SPB = 1, int WSPLIT = (FM == 2 ? 2 : 1)>
 static hipError_t launch_tile(GemmArgs a, hipStream_t st)
 {
     constexpr int NA = EPI == EPI_GATE ? 2 : 1;
@@ -421,10 +457,10 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t st)
     static_assert(lds <= 160 * 1024, "LDS budget");
     a.n_tiles = (int)ceil_div(a.n, 32 * FN);
     a.m_tiles = (int)ceil_div(a.m, 128 * FM);
-    const auto kern = gemm_kernel<FM, FN, EPI, DB, SPB>;
+    const auto kern = gemm_kernel<FM, FN, EPI, DB, SPB, WSPLIT>;
     static LdsLimit lim;
     if (hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds, lim)) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_tiles * a.m_tiles)), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_tiles * a.m_tiles)), dim3(kThreads * WSPLIT), lds, st, a);
     return hipGetLastError();
 }
 

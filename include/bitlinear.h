@@ -194,6 +194,11 @@ bl_status bitlinear_forward_norm(const void *x, bl_dtype dtype, int64_t m, int64
  *            NULL skips it
  *   workspace  >= bitlinear_workspace_size(BL_OP_FORWARD, m, k, n) bytes
  * Requires k % 4 == 0. No bias (the layer has none: section 架构创新).
+ * Cost note: the kernels read weight rows padded to a multiple of 64 inputs.
+ * When k % 64 != 0 the workspace also holds such a padded copy of `packed`,
+ * rewritten on every call (one extra n*k/4-byte read and write); the same
+ * holds for bitlinear_ffn (hidden or ffn not a multiple of 64) and the
+ * variants below.
  */
 bl_status bitlinear_forward(const void *x, bl_dtype dtype, int64_t m, int64_t k,
                             const uint8_t *packed, const float *gamma, int64_t n,
