@@ -447,8 +447,12 @@ __global__ __launch_bounds__(256 * WSPLIT) void gemm_kernel(GemmArgs a)
     }
 }
 
-// 256-token tiles run with eight waves (two per SIMD, the fragments split)
-template <int FM, int FN, int EPI, int DB, int SPB = 1, int WSPLIT = (FM == 2 ? 2 : 1)>
+// Eight waves (two per SIMD, the fragments split) except for the 128-token
+// tiles of a gate/up pair: same-box A/B at 2048 tokens, eight waves took the
+// prefill layers 48.6 / 47.5 against 51.1 / 50.2 us (256x224 and 128x160
+// tiles) and the 8B gate/up pair's 256x128 tiles 356 against 367.5 us per FFN,
+// but its 128x128 tiles 364.5 against 357 us
+template <int FM, int FN, int EPI, int DB, int SPB = 1, int WSPLIT = (FM == 2 || EPI != EPI_GATE ? 2 : 1)>
 static hipError_t launch_tile(GemmArgs a, hipStream_t st)
 {
     constexpr int NA = EPI == EPI_GATE ? 2 : 1;
