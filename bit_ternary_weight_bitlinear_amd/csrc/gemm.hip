@@ -491,15 +491,15 @@ struct TileShape {
 };
 static bool tile_allowed(int fm, int fn, int na)
 {
-    if (na == 2) return (fm == 1 && fn <= 6) || (fm == 2 && fn == 4);
-    return fm * fn <= 14;
+    if (na == 2) return (fm == 1 && fn >= 4 && fn <= 6) || (fm == 2 && (fn == 4 || fn == 2));
+    return fn >= 4 && fm * fn <= 14;
 }
 static int64_t tile_count(int64_t m, int64_t n, int fm, int fn) { return ceil_div(n, 32 * fn) * ceil_div(m, 128 * fm); }
 static TileShape pick_tile(int64_t m, int64_t n, int na)
 {
     TileShape best{1, 4, 1e300};
     for (int fm = 2; fm >= 1; --fm)
-        for (int fn = 8; fn >= 4; --fn) {
+        for (int fn = 8; fn >= 2; --fn) {
             if (!tile_allowed(fm, fn, na)) continue;
             const int64_t rounds = ceil_div(tile_count(m, n, fm, fn), 256);
             const double cost = (double)rounds * (fm * fn * na * (1.0 + 0.2 / fm) + 3.0);
@@ -549,7 +549,10 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
         default: return launch_fm1<8, EPI>(a, st);
         }
     } else {
-        if (t.fm == 2) return launch_tile<2, 4, EPI, 5>(a, st);  // 138 KB of LDS
+        if (t.fm == 2) {  // 138 KB of LDS
+            if (t.fn == 2) return launch_tile<2, 2, EPI, 5>(a, st);
+            return launch_tile<2, 4, EPI, 5>(a, st);
+        }
         switch (t.fn) {
         case 4: return launch_tile<1, 4, EPI, 8>(a, st);
         case 5: return launch_tile<1, 5, EPI, 8>(a, st);

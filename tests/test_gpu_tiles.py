@@ -29,13 +29,13 @@ def pick_tile(m, n, na):
     """Mirror of the host-side tile choice: least rounds over 256 CUs times the
     per-tile cost (MFMA blocks, their weight expansion, a fixed per-step term),
     among shapes with at most 14 (one matrix) accumulator blocks, or for the
-    gate/up pair 12 on 128-token tiles or the 256x128 tile."""
+    gate/up pair 12 on 128-token tiles or the 256x128 and 256x64 tiles."""
     best, best_cost = (1, 4), math.inf
     for fm in (2, 1):
-        for fn in range(8, 3, -1):
-            if na == 2 and not ((fm == 1 and fn <= 6) or (fm == 2 and fn == 4)):
+        for fn in range(8, 1, -1):
+            if na == 2 and not ((fm == 1 and 4 <= fn <= 6) or (fm == 2 and fn in (2, 4))):
                 continue
-            if na == 1 and fm * fn > 14:
+            if na == 1 and (fn < 4 or fm * fn > 14):
                 continue
             tiles = math.ceil(n / (32 * fn)) * math.ceil(m / (128 * fm))
             cost = math.ceil(tiles / 256) * (fm * fn * na * (1.0 + 0.2 / fm) + 3.0)
@@ -60,7 +60,7 @@ def ragged_shape(fm, fn, na):
 
 
 SINGLE = [(2, 4), (2, 5), (2, 6), (2, 7), (1, 4), (1, 5), (1, 6), (1, 7), (1, 8)]
-PAIR = [(1, 4), (1, 5), (1, 6), (2, 4)]
+PAIR = [(1, 4), (1, 5), (1, 6), (2, 4), (2, 2)]
 
 
 @pytest.fixture(scope="module")
