@@ -436,7 +436,6 @@ __global__ __launch_bounds__(256 * WSPLIT) void gemm_kernel(GemmArgs a)
     const int id = blockIdx.x, xcd = id & 7, per = tiles >> 3, rem = tiles & 7;
     const int tile = xcd * per + min(xcd, rem) + (id >> 3);
     const int64_t m0 = (int64_t)(tile / a.n_tiles) * BM, n0 = (int64_t)(tile % a.n_tiles) * BN;
-    const int nks = (int)(a.kp / 64);
 
     if constexpr (WSPLIT == 1) {
         gemm_waves<FM, FN, EPI, DB, SPB, 4, FN, 0, true>(a, smem, wave, m0, n0);
@@ -472,8 +471,8 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t st)
 template <int FN, int EPI>
 static hipError_t launch_fm1(const GemmArgs &a, hipStream_t st)
 {
-    if ((a.kp / 64) % 2 == 0) return launch_tile<1, FN, EPI, 5, 2>(a, st);
-    return launch_tile<1, FN, EPI, 8, 1>(a, st);
+    if ((a.kp / 64) % 2 == 0) return launch_tile<1, FN, EPI, 3, 2>(a, st);
+    return launch_tile<1, FN, EPI, 6, 1>(a, st);
 }
 
 // Tile shape: the (FM, FN) of least cost, rounds over the 256 CUs times a
@@ -527,6 +526,10 @@ static int64_t split_columns(int64_t m, int64_t n, int na)
     return split < t.cost ? n_main : n;
 }
 
+// Ring depths (stages requested ahead): with eight waves per workgroup the
+// shallower rings measured faster (same-box A/B at 2048 tokens: prefill step
+// 0.0940 against 0.0955 ms with DB 4 / 3 instead of 6 / 5; 8B FFN 351.5
+// against 353 us with DB 4 instead of 5 and 6)
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
 {
@@ -535,10 +538,10 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
     if constexpr (NA == 1) {
         if (t.fm == 2) {
             switch (t.fn) {
-            case 4: return launch_tile<2, 4, EPI, 6>(a, st);
-            case 5: return launch_tile<2, 5, EPI, 6>(a, st);
-            case 6: return launch_tile<2, 6, EPI, 6>(a, st);
-            default: return launch_tile<2, 7, EPI, 6>(a, st);
+            case 4: return launch_tile<2, 4, EPI, 4>(a, st);
+            case 5: return launch_tile<2, 5, EPI, 4>(a, st);
+            case 6: return launch_tile<2, 6, EPI, 4>(a, st);
+            default: return launch_tile<2, 7, EPI, 4>(a, st);
             }
         }
         switch (t.fn) {
@@ -549,9 +552,9 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
         default: return launch_fm1<8, EPI>(a, st);
         }
     } else {
-        if (t.fm == 2) {  // 138 KB of LDS
-            if (t.fn == 2) return launch_tile<2, 2, EPI, 5>(a, st);
-            return launch_tile<2, 4, EPI, 5>(a, st);
+        if (t.fm == 2) {  // 114 KB of LDS
+            if (t.fn == 2) return launch_tile<2, 2, EPI, 4>(a, st);
+            return launch_tile<2, 4, EPI, 4>(a, st);
         }
         switch (t.fn) {
         case 4: return launch_tile<1, 4, EPI, 8>(a, st);
