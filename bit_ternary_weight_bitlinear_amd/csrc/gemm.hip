@@ -9,7 +9,8 @@
 //    eight waves, two per SIMD: waves w and w+4 take the same tokens, one the
 //    first (FN+1)/2 feature fragments and the other the rest, so while one
 //    waits at a barrier or for LDS the other keeps the SIMD's matrix core busy
-//    (same MFMA work per SIMD, half the accumulators per wave);
+//    (same MFMA work per SIMD, half the accumulators per wave); 256x224
+//    tiles run sixteen waves, four per SIMD, in four fragment groups;
 //  * two LDS rings, filled by direct global->LDS loads (global_load_lds_dwordx4)
 //    issued DB k-steps ahead: the qperm activation tile of each 64-input step
 //    (64-byte rows) and the packed weight rows of that step (16-byte rows).
@@ -169,9 +170,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const v16i (&acc)[
 // wave has all FN fragments; with NW = 8 (two waves per SIMD) waves 0-3 take
 // the first (FN+1)/2 fragments and waves 4-7 the rest, so each SIMD keeps the
 // same MFMA work with half the accumulators per wave, and one wave's barrier
-// and LDS waits can be covered by the other's MFMAs. The direct loads of a
-// step are spread over all NW waves (the packed weight rows over waves 0-3:
-// WLOAD). SPB: 64-input steps per ring stage (1 or 2). With 2, the direct
+// and LDS waits can be covered by the other's MFMAs; NW = 16 (four waves per
+// SIMD) splits the fragments into four groups the same way. The direct loads
+// of a step are spread over all NW waves (the packed weight rows over waves
+// 0-3: WLOAD). SPB: 64-input steps per ring stage (1 or 2). With 2, the direct
 // loads of a stage go out once per pair of steps and the barrier runs once per
 // pair; the step count must be even. DB: stages requested ahead.
 template <int FM, int FN, int EPI, int DB, int SPB, int NW, int FW, int FOFF, bool WLOAD>
@@ -181,7 +183,9 @@ __device__ __forceinline__ void gemm_waves(const GemmArgs &a, int8_t *smem, int 
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int BM = 128 * FM, BN = 32 * FN, WM = 32 * FM;
     static_assert(FM * FW * NA <= 16, "accumulators fit the 256 AGPRs");
-    static_assert(NW == 4 || (NW == 8 && FM * FW * NA <= 8), "two waves per SIMD: half the accumulators");
+    static_assert(NW == 4 || (NW == 8 && FM * FW * NA <= 8) || (NW == 16 && FM * FW * NA <= 4),
+                  "two or four waves per SIMD: a half or a quarter of the accumulators");
+    static_assert(FW >= 1, "every wave owns at least one fragment");
     static_assert(BN <= 256, "packed rows: one 64-row direct load per wave");
     static_assert(DB >= 3, "at least one stage of slack for the direct loads");
     static_assert(SPB == 1 || SPB == 2, "one or two steps per stage");
@@ -439,10 +443,19 @@ __global__ __launch_bounds__(256 * WSPLIT) void gemm_kernel(GemmArgs a)
 
     if constexpr (WSPLIT == 1) {
         gemm_waves<FM, FN, EPI, DB, SPB, 4, FN, 0, true>(a, smem, wave, m0, n0);
-    } else {
+    } else if constexpr (WSPLIT == 2) {
         constexpr int F0 = (FN + 1) / 2;
         if (wave < 4) gemm_waves<FM, FN, EPI, DB, SPB, 8, F0, 0, true>(a, smem, wave, m0, n0);
         else gemm_waves<FM, FN, EPI, DB, SPB, 8, FN - F0, F0, false>(a, smem, wave, m0, n0);
+    } else {
+        // sixteen waves, four per SIMD: fragment groups of F, F, F and FN - 3F
+        constexpr int F = (FN + 3) / 4;
+        static_assert(WSPLIT == 4 && FN > 3 * F, "four non-empty fragment groups");
+        const int g = wave >> 2;
+        if (g == 0) gemm_waves<FM, FN, EPI, DB, SPB, 16, F, 0, true>(a, smem, wave, m0, n0);
+        else if (g == 1) gemm_waves<FM, FN, EPI, DB, SPB, 16, F, F, false>(a, smem, wave, m0, n0);
+        else if (g == 2) gemm_waves<FM, FN, EPI, DB, SPB, 16, F, 2 * F, false>(a, smem, wave, m0, n0);
+        else gemm_waves<FM, FN, EPI, DB, SPB, 16, FN - 3 * F, 3 * F, false>(a, smem, wave, m0, n0);
     }
 }
 
@@ -526,6 +539,10 @@ static int64_t split_columns(int64_t m, int64_t n, int na)
     return split < t.cost ? n_main : n;
 }
 
+// 256x224 tiles run sixteen waves, four per SIMD, in fragment groups of 2, 2,
+// 2 and 1 (same-box A/B, prefill 2560->6912 layer at 2048 tokens: 46.7
+// against 48.6 us with eight waves); 256x128 tiles keep eight (sixteen: the
+// 8B FFN at 2048 tokens 379-387 against 360-366 us).
 // Ring depths (stages requested ahead): with eight waves per workgroup the
 // shallower rings measured faster (same-box A/B at 2048 tokens: prefill step
 // 0.0940 against 0.0955 ms with DB 4 / 3 instead of 6 / 5; 8B FFN 351.5
@@ -541,7 +558,7 @@ static hipError_t launch_epi(const GemmArgs &a, hipStream_t st)
             case 4: return launch_tile<2, 4, EPI, 4>(a, st);
             case 5: return launch_tile<2, 5, EPI, 4>(a, st);
             case 6: return launch_tile<2, 6, EPI, 4>(a, st);
-            default: return launch_tile<2, 7, EPI, 4>(a, st);
+            default: return launch_tile<2, 7, EPI, 4, 1, 4>(a, st);  // sixteen waves
             }
         }
         switch (t.fn) {
