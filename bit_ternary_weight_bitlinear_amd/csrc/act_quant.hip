@@ -68,57 +68,6 @@ __device__ inline void store_nat(int8_t *row, int64_t k, int64_t g, const uint4 
         if (16 * g + 4 * j < k) p[j] = d[j];
 }
 
-// a + b = s + e exactly (Knuth's TwoSum)
-__device__ inline void two_sum(double a, double b, double &s, double &e)
-{
-    s = a + b;
-    const double bb = s - a;
-    e = (a - (s - bb)) + (b - bb);
-}
-
-// double-double accumulation of one value
-__device__ inline void dd_add(double &hi, double &lo, double v)
-{
-    double e;
-    two_sum(hi, v, hi, e);
-    lo += e;
-}
-
-// double-double sum over the workgroup (xor butterfly in each wave, then the
-// four wave results in order through LDS); every thread gets the fp64 result
-__device__ inline double block_sum_dd(double hi, double lo, double *red)
-{
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) {
-        const double ph = __shfl_xor(hi, mask, 64);
-        const double pl = __shfl_xor(lo, mask, 64);
-        double e;
-        two_sum(hi, ph, hi, e);
-        lo = lo + pl + e;
-    }
-    if ((threadIdx.x & 63) == 0) {
-        red[2 * (threadIdx.x >> 6)] = hi;
-        red[2 * (threadIdx.x >> 6) + 1] = lo;
-    }
-    __syncthreads();
-    double h = red[0], l = red[1];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-        double e;
-        two_sum(h, red[2 * w], h, e);
-        l = l + red[2 * w + 1] + e;
-    }
-    return h + l;
-}
-
-// the per-token factor r = 1 / sqrt(fp32(S / k) + 1e-5)
-__device__ inline float norm_factor(double ssq, int64_t k)
-{
-    const float ms = (float)(ssq / (double)k);
-    const float d = ms + kEps;
-    return 1.0f / sqrtf(d);
-}
-
 // x^ = (x * r) * g for the 16 inputs of group g (gain entries past k unused)
 template <bool GAIN>
 __device__ inline void normalize_group(float f[16], float r, const float *gain, int64_t k, int64_t g)
@@ -258,7 +207,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const T *__restrict__ x,
                 sq(f);
             }
         }
-        r_norm = norm_factor(block_sum_dd(hi, lo, red_d), k);
+        r_norm = norm_factor(block_sum_dd<4>(hi, lo, red_d), k);
     }
     float amax = 0.0f;
     if (resident) {

@@ -246,6 +246,60 @@ __device__ inline void load_group(const T *row, int64_t k, int64_t g, float f[16
     }
 }
 
+// ---------------------------------------------------------------- RMS norm (subln)
+// a + b = s + e exactly (Knuth's TwoSum)
+__device__ inline void two_sum(double a, double b, double &s, double &e)
+{
+    s = a + b;
+    const double bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+
+// double-double accumulation of one value
+__device__ inline void dd_add(double &hi, double &lo, double v)
+{
+    double e;
+    two_sum(hi, v, hi, e);
+    lo += e;
+}
+
+// double-double sum over a workgroup of NW waves (xor butterfly in each wave,
+// then the wave results in order through LDS, red[2 * NW]); every thread gets
+// the fp64 result
+template <int NW>
+__device__ inline double block_sum_dd(double hi, double lo, double *red)
+{
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        const double ph = __shfl_xor(hi, mask, 64);
+        const double pl = __shfl_xor(lo, mask, 64);
+        double e;
+        two_sum(hi, ph, hi, e);
+        lo = lo + pl + e;
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[2 * (threadIdx.x >> 6)] = hi;
+        red[2 * (threadIdx.x >> 6) + 1] = lo;
+    }
+    __syncthreads();
+    double h = red[0], l = red[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        double e;
+        two_sum(h, red[2 * w], h, e);
+        l = l + red[2 * w + 1] + e;
+    }
+    return h + l;
+}
+
+// the per-token factor r = 1 / sqrt(fp32(S / k) + 1e-5)
+__device__ inline float norm_factor(double ssq, int64_t k)
+{
+    const float ms = (float)(ssq / (double)k);
+    const float d = ms + kEps;
+    return 1.0f / sqrtf(d);
+}
+
 // Per-token int8 code q = clamp(rint(v * inv), -127, 127), with inv = 127 / s and
 // s >= max|v|. Since |v * inv| <= 127 * (1 + 2^-23) after rounding, rint never
 // leaves [-127, 127] and the clamp cannot bind. The rounding is done by adding

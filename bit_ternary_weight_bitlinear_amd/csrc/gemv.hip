@@ -53,6 +53,7 @@ struct GemvArgs {
     float qmax;               // code of the largest magnitude (127; 12 for doubled E2M1 codes)
     int rows_per_wg;  // R
     int chunks;       // kp / 64
+    const float *gain;  // NORM: per-input gain [k], or NULL (last: the other fields keep their offsets)
 };
 
 // LDS slot of activation group (c, d): 16-byte slots rotated by (c >> 2) & 3 so
@@ -65,10 +66,16 @@ __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) &
 // units per lane group. PREQ: x holds quantized rows [m][kp] in the qperm
 // order (with pre_s and pre_sumq) written by a quantization kernel: their
 // 16-byte words go to LDS as they are, one barrier, no quantization.
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false>
+// NORM: one token whose activations are first RMS-normalized (subln): x^ =
+// (x * r) * g with r = 1 / sqrt(fp32(S / k) + 1e-5), S = sum x^2 as an fp64
+// double-double sum over the workgroup, g the optional per-input gain (none:
+// x^ = x * r); then the same quantization and product.
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false,
+          bool NORM = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
     static_assert(!PREQ || (RES && FULL && !DUAL), "quantized rows: resident slots, one matrix");
+    static_assert(!NORM || (RES && FULL && !DUAL && !PREQ && MT == 1), "normalized decode: one token, one matrix");
     constexpr int NA = DUAL ? 2 : 1;
     extern __shared__ __align__(16) int8_t lds[];  // q [MT][kp], then int32 sums [NA][MT][R]
     __shared__ float red_f[MT][kGW];
@@ -126,6 +133,18 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
                                   : reinterpret_cast<const uint4 *>(x + slot_t[s] * a.k + 16 * (int64_t)slot_g[s]);
 #pragma unroll
             for (int q = 0; q < XQ; ++q) xq[s][q] = p[q];
+        }
+    }
+    // the gain entries of the slots' inputs, requested with the activations
+    float4 gq[NORM ? SL : 1][4];
+    if constexpr (NORM) {
+        if (a.gain) {
+#pragma unroll
+            for (int s = 0; s < SL; ++s) {
+                const float4 *gp = reinterpret_cast<const float4 *>(a.gain + 16 * (int64_t)slot_g[s]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gq[s][j] = gp[j];
+            }
         }
     }
     float xr[SL][16];
@@ -203,6 +222,34 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
         }
         __syncthreads();
     } else {
+        if constexpr (NORM) {
+            // S over this thread's groups (slots past the last group re-read
+            // it and are skipped here), then over the workgroup
+            __shared__ double red_d[2 * kGW];
+            double hi = 0.0, lo = 0.0;
+#pragma unroll
+            for (int s = 0; s < SL; ++s)
+                if (tid + s * kGT < NG) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) dd_add(hi, lo, (double)xr[s][j] * (double)xr[s][j]);
+                }
+            const float r = norm_factor(block_sum_dd<kGW>(hi, lo, red_d), a.k);
+            const bool has_gain = a.gain != nullptr;
+#pragma unroll
+            for (int s = 0; s < SL; ++s) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xr[s][j] = xr[s][j] * r;
+                if (has_gain) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        xr[s][4 * j + 0] = xr[s][4 * j + 0] * gq[s][j].x;
+                        xr[s][4 * j + 1] = xr[s][4 * j + 1] * gq[s][j].y;
+                        xr[s][4 * j + 2] = xr[s][4 * j + 2] * gq[s][j].z;
+                        xr[s][4 * j + 3] = xr[s][4 * j + 3] * gq[s][j].w;
+                    }
+                }
+            }
+        }
         float amax[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
@@ -450,10 +497,24 @@ bool gemv_supported(int64_t m, int64_t kp)
 
 namespace {
 
-template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false>
+template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false,
+          bool NORM = false>
 void launch_one(dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL, PREQ>), grid, dim3(kGT), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL, PREQ, NORM>), grid, dim3(kGT), lds, st, a);
+}
+
+// one bf16 token, RMS-normalized in the prologue
+template <int SL>
+void launch_norm(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    if (jm <= 1) launch_one<bf16_t, 1, false, true, true, 1, SL, false, true>(grid, lds, st, a);
+    else if (jm <= 2) launch_one<bf16_t, 1, false, true, true, 2, SL, false, true>(grid, lds, st, a);
+    else if (jm <= 3) launch_one<bf16_t, 1, false, true, true, 3, SL, false, true>(grid, lds, st, a);
+    else if (jm <= 4) launch_one<bf16_t, 1, false, true, true, 4, SL, false, true>(grid, lds, st, a);
+    else if (jm <= 6) launch_one<bf16_t, 1, false, true, true, 6, SL, false, true>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<bf16_t, 1, false, true, true, 8, SL, false, true>(grid, lds, st, a);
+    else launch_one<bf16_t, 1, false, true, true, 16, SL, false, true>(grid, lds, st, a);
 }
 
 // single token, whole groups, activations resident: the decode hot path, with
@@ -534,6 +595,11 @@ bool gemv_prequant_supported(int64_t m, int64_t kp)
     return gemv_supported(m, kp) && m * (kp / 16) <= (int64_t)kSlots * kGT;
 }
 
+bool gemv_norm_supported(int64_t m, int64_t k, bool bf16)
+{
+    return m == 1 && bf16 && k % 16 == 0 && gemv_supported(1, round_up(k, 64)) && k / 16 <= (int64_t)kSlots * kGT;
+}
+
 namespace {
 
 template <int MT, int SL>
@@ -566,6 +632,7 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out; a.q_out = p.q_out; a.s_out = p.s_out;
     a.hmax_part = p.hmax_part; a.pre_s = p.pre_s; a.pre_sumq = p.pre_sumq; a.qmax = p.qmax;
+    a.gain = p.gain;
     a.chunks = (int)(p.kp / 64);
     const bool dual = p.w1 != nullptr;
     const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);
@@ -578,6 +645,13 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
         if (sl <= 1) launch_preq<1>((int)p.m, jm, grid, lds, st, a);
         else if (sl <= 2) launch_preq<2>((int)p.m, jm, grid, lds, st, a);
         else launch_preq<4>((int)p.m, jm, grid, lds, st, a);
+        return hipGetLastError();
+    }
+    if (p.norm) {  // one bf16 token, normalized in the prologue (gemv_norm_supported)
+        const int64_t sl = ceil_div(p.k / 16, (int64_t)kGT);
+        if (sl <= 1) launch_norm<1>(jm, grid, lds, st, a);
+        else if (sl <= 2) launch_norm<2>(jm, grid, lds, st, a);
+        else launch_norm<4>(jm, grid, lds, st, a);
         return hipGetLastError();
     }
     if (p.bf16) {

@@ -451,6 +451,22 @@ def test_forward_norm(bl, m, k, n):
     assert_y_close(host(y), r["y"])
 
 
+# One bf16 token: the norm runs in the decode kernel's prologue (fp64 sum of
+# squares over its 512 threads), with and without the gain, k with a ragged
+# 64-input block, and up to four resident 16-input groups per thread.
+@pytest.mark.parametrize("k,n,gain", [(2576, 300, True), (16384, 100, False), (20000, 64, True), (64, 8, False),
+                                      (6912, 2560, False)])
+def test_forward_norm_decode(bl, k, n, gain):
+    w, p_ref, g_ref, _ = make_linear(144, 1, n, k)
+    x = synth.activations(144, 1, k, dtype="bf16", outlier_channels=3, outlier_scale=20.0)
+    g = (1.0 + 0.25 * synth.normal(145, k)).astype(np.float32) if gain else None
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward_norm(to_dev(x, "bf16"), packed, gamma, to_dev(g) if gain else None, return_acc=True)
+    r = oracle.forward_norm(x, p_ref, g_ref, k, "bf16", g)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
+
+
 # ------------------------------------------------------------------ decode FFN skipping zero channels of h
 
 @pytest.mark.parametrize("n,k", [(4, 4), (8, 260), (300, 512), (4096, 14336)])
