@@ -371,6 +371,13 @@ bl_status bitlinear_forward_a4(const void *x, bl_dtype dtype, int64_t m, int64_t
         if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
         w = L.wpad;
     }
+    if (gemv_norm_supported(m, k, dtype == BL_BF16)) {  // one token: the 4-bit codes in the decode kernel's prologue
+        GemvProblem p{};
+        p.x = x; p.bf16 = true; p.m = m; p.k = k; p.kp = L.kp; p.n = n;
+        p.w0 = w; p.ldw = L.kp / 4; p.gamma0 = gamma; p.out = y; p.acc_out = acc_out;
+        p.a4 = true; p.keep = keep; p.qmax = 12.0f;
+        return hip_status(launch_gemv(p, st));
+    }
     if (hipError_t e = launch_act_quant_a4(x, dtype == BL_BF16, m, k, L.kp, keep, nullptr, L.qp, L.s, L.sumq, st))
         return hip_status(e);
     return prequant_contraction(L, m, k, n, w, gamma, y, acc_out, 12.0f, st);

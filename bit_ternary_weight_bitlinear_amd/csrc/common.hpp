@@ -246,6 +246,70 @@ __device__ inline void load_group(const T *row, int64_t k, int64_t g, float f[16
     }
 }
 
+// ---------------------------------------------------------------- 4-bit activations (E2M1, top-K)
+// The nearest E2M1 value of v (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives),
+// doubled; at a midpoint the value with mantissa bit 0 (0, 1, 2, 4) wins.
+// The E2M1 values step by 0.5 below 2, by 1 below 4 and by 2 above, so the
+// doubled code is rint(|v| * 2 / d) * d with d = 1, 2, 4 in those ranges
+// (|v| times a power of two is exact, and rint's ties to even are exactly the
+// midpoint rule), capped at 12: no branches, and NaN gives 12.
+__device__ inline int e2m1_doubled(float v)
+{
+    const float a = fabsf(v);
+    const float up = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    const float d = a < 2.0f ? 1.0f : (a < 4.0f ? 2.0f : 4.0f);
+    const int c = (int)fminf(rintf(a * up) * d, 12.0f);
+    return v < 0.0f ? -c : c;
+}
+
+// inclusive prefix sum over the 64 lanes: Kogge-Stone steps of 1, 2, 4 and 8
+// inside each 16-lane row (row_shr, lanes with no source add 0), then the row
+// broadcasts carry each row's total into the rows above it
+__device__ inline int wave_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+    return v;
+}
+
+constexpr int kDigitBits = 11;
+constexpr int kDigitBins = 1 << kDigitBits;
+
+// The digit of the want-th largest candidate, from a histogram h of
+// kDigitBins bins (bins past the digit's range hold 0); want becomes the rank
+// of tau among the candidates that share that digit. Every wave computes it
+// alone, with no barrier: lane L sums bins 32L .. 32L+31 (read in a rotated
+// order to spread the LDS banks), a prefix sum over the lanes gives each lane
+// the count above its range and so the lane whose range holds the want-th
+// largest, and a second prefix sum over that lane's 32 bins gives the bin.
+__device__ inline uint32_t pick_digit(const int *h, int &want)
+{
+    const int lane = threadIdx.x & 63;
+    const int4 *hp = reinterpret_cast<const int4 *>(h + 32 * lane);
+    int sl = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int4 c = hp[(i + lane) & 7];
+        sl += c.x + c.y + c.z + c.w;
+    }
+    const int pl = wave_scan(sl);
+    const int above = __builtin_amdgcn_readlane(pl, 63) - pl;  // candidates in the lanes above
+    const uint64_t b1 = __ballot(above < want && want <= above + sl);
+    const int ls = b1 ? __builtin_ctzll(b1) : 0;
+    const int base = __builtin_amdgcn_readlane(above, ls);
+    const int c = lane < 32 ? h[32 * ls + lane] : 0;
+    const int p2 = wave_scan(c);
+    const int ge = base + __builtin_amdgcn_readlane(p2, 31) - p2 + c;  // candidates with digit >= 32 ls + lane
+    const uint64_t b2 = __ballot(lane < 32 && ge >= want && ge - c < want);
+    const int lj = b2 ? __builtin_ctzll(b2) : 0;
+    want -= __builtin_amdgcn_readlane(ge - c, lj);
+    return (uint32_t)(32 * ls + lj);
+}
+
 // ---------------------------------------------------------------- RMS norm (subln)
 // a + b = s + e exactly (Knuth's TwoSum)
 __device__ inline void two_sum(double a, double b, double &s, double &e)

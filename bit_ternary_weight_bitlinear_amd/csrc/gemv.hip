@@ -54,6 +54,7 @@ struct GemvArgs {
     int rows_per_wg;  // R
     int chunks;       // kp / 64
     const float *gain;  // NORM: per-input gain [k], or NULL (last: the other fields keep their offsets)
+    int keep;           // A4: entries kept per token
 };
 
 // LDS slot of activation group (c, d): 16-byte slots rotated by (c >> 2) & 3 so
@@ -70,12 +71,19 @@ __device__ inline int lds_slot(int c, int d) { return c * 64 + ((d ^ ((c >> 2) &
 // (x * r) * g with r = 1 / sqrt(fp32(S / k) + 1e-5), S = sum x^2 as an fp64
 // double-double sum over the workgroup, g the optional per-input gain (none:
 // x^ = x * r); then the same quantization and product.
+// A4: one token quantized to 4-bit E2M1 codes instead (the a.keep largest
+// |x| kept, v = x * (6 / s) to the nearest E2M1 value, stored doubled): tau,
+// the keep-th largest |x|, by a radix select over the workgroup (two 11-bit
+// digit passes for bf16, histograms in LDS), the same select as the 4-bit
+// quantization kernel, so the codes are the same.
 template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false,
-          bool NORM = false>
+          bool NORM = false, bool A4 = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 {
     static_assert(!PREQ || (RES && FULL && !DUAL), "quantized rows: resident slots, one matrix");
     static_assert(!NORM || (RES && FULL && !DUAL && !PREQ && MT == 1), "normalized decode: one token, one matrix");
+    static_assert(!A4 || (RES && FULL && !DUAL && !PREQ && MT == 1 && !NORM && sizeof(T) == 2),
+                  "4-bit decode: one bf16 token, one matrix");
     constexpr int NA = DUAL ? 2 : 1;
     extern __shared__ __align__(16) int8_t lds[];  // q [MT][kp], then int32 sums [NA][MT][R]
     __shared__ float red_f[MT][kGW];
@@ -250,6 +258,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
                 }
             }
         }
+        // 4-bit: the select's histograms, zeroed here and published by the
+        // absmax barrier below (bf16: bits 30..20, then 19..16)
+        constexpr int kA4Passes = 2;
+        int *hist = nullptr;  // [kA4Passes][kDigitBins]
+        if constexpr (A4) {
+            __shared__ __align__(16) int hist_lds[kA4Passes * kDigitBins];
+            hist = hist_lds;
+            for (int i = tid; i < kA4Passes * kDigitBins / 4; i += kGT)
+                reinterpret_cast<int4 *>(hist)[i] = make_int4(0, 0, 0, 0);
+        }
         float amax[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) amax[t] = 0.0f;
@@ -288,12 +306,50 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a)
 #pragma unroll
             for (int w = 1; w < kGW; ++w) mx = fmaxf(mx, red_f[t][w]);
             st[t] = fmaxf(mx, kEps);
-            inv[t] = 127.0f / st[t];
+            inv[t] = (A4 ? 6.0f : 127.0f) / st[t];
             qs[t] = 0;
+        }
+        uint32_t tau = 0;  // 4-bit: the keep-th largest |x| (as bits)
+        if constexpr (A4) {
+            uint32_t prefix = 0, pmask = 0;
+            int want = a.keep;
+#pragma unroll
+            for (int p = 0; p < kA4Passes; ++p) {
+                const int hi = 31 - p * kDigitBits;
+                const int lo = hi - kDigitBits > 16 ? hi - kDigitBits : 16;
+                const uint32_t dmask = (1u << (hi - lo)) - 1u;
+                int *h = hist + p * kDigitBins;
+#pragma unroll
+                for (int s = 0; s < SL; ++s)
+                    if (tid + s * kGT < NG) {  // slots past the last group re-read it: not counted
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const uint32_t key = __float_as_uint(fabsf(xr[s][j]));
+                            if ((key & pmask) == prefix) atomicAdd(&h[(key >> lo) & dmask], 1);
+                        }
+                    }
+                __syncthreads();
+                prefix |= pick_digit(h, want) << lo;
+                pmask |= dmask << lo;
+            }
+            tau = prefix;
         }
         auto emit = [&](int t, int g, const float f[16], float iv) {
             uint4 pv, nv;
-            const int sum = quant_group(f, iv, &pv, &nv);
+            int sum;
+            if constexpr (A4) {
+                int qi[16];
+                sum = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    qi[j] = __float_as_uint(fabsf(f[j])) >= tau ? e2m1_doubled(f[j] * iv) : 0;
+                    sum += qi[j];
+                }
+                pv = qperm_pack(qi);
+                nv = make_uint4(0, 0, 0, 0);  // no natural-order copy (q_out is not used in this mode)
+            } else {
+                sum = quant_group(f, iv, &pv, &nv);
+            }
 #pragma unroll
             for (int u = 0; u < MT; ++u)
                 if (u == t) qs[u] += sum;
@@ -498,10 +554,23 @@ bool gemv_supported(int64_t m, int64_t kp)
 namespace {
 
 template <typename T, int MT, bool DUAL, bool RES, bool FULL, int JM, int SL = kSlots, bool PREQ = false,
-          bool NORM = false>
+          bool NORM = false, bool A4 = false>
 void launch_one(dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
 {
-    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL, PREQ, NORM>), grid, dim3(kGT), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<T, MT, DUAL, RES, FULL, JM, SL, PREQ, NORM, A4>), grid, dim3(kGT), lds, st, a);
+}
+
+// one bf16 token, quantized to 4-bit E2M1 codes in the prologue
+template <int SL>
+void launch_a4(int jm, dim3 grid, size_t lds, hipStream_t st, const GemvArgs &a)
+{
+    if (jm <= 1) launch_one<bf16_t, 1, false, true, true, 1, SL, false, false, true>(grid, lds, st, a);
+    else if (jm <= 2) launch_one<bf16_t, 1, false, true, true, 2, SL, false, false, true>(grid, lds, st, a);
+    else if (jm <= 3) launch_one<bf16_t, 1, false, true, true, 3, SL, false, false, true>(grid, lds, st, a);
+    else if (jm <= 4) launch_one<bf16_t, 1, false, true, true, 4, SL, false, false, true>(grid, lds, st, a);
+    else if (jm <= 6) launch_one<bf16_t, 1, false, true, true, 6, SL, false, false, true>(grid, lds, st, a);
+    else if (jm <= 8) launch_one<bf16_t, 1, false, true, true, 8, SL, false, false, true>(grid, lds, st, a);
+    else launch_one<bf16_t, 1, false, true, true, 16, SL, false, false, true>(grid, lds, st, a);
 }
 
 // one bf16 token, RMS-normalized in the prologue
@@ -632,7 +701,7 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
     a.gamma0 = p.gamma0; a.gamma1 = p.gamma1;
     a.out = p.out; a.acc_out = p.acc_out; a.q_out = p.q_out; a.s_out = p.s_out;
     a.hmax_part = p.hmax_part; a.pre_s = p.pre_s; a.pre_sumq = p.pre_sumq; a.qmax = p.qmax;
-    a.gain = p.gain;
+    a.gain = p.gain; a.keep = (int)p.keep;
     a.chunks = (int)(p.kp / 64);
     const bool dual = p.w1 != nullptr;
     const int64_t r = gemv_rows_per_wg(p.n, a.chunks, dual);
@@ -645,6 +714,13 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
         if (sl <= 1) launch_preq<1>((int)p.m, jm, grid, lds, st, a);
         else if (sl <= 2) launch_preq<2>((int)p.m, jm, grid, lds, st, a);
         else launch_preq<4>((int)p.m, jm, grid, lds, st, a);
+        return hipGetLastError();
+    }
+    if (p.a4) {  // one bf16 token, 4-bit codes made in the prologue (gemv_norm_supported)
+        const int64_t sl = ceil_div(p.k / 16, (int64_t)kGT);
+        if (sl <= 1) launch_a4<1>(jm, grid, lds, st, a);
+        else if (sl <= 2) launch_a4<2>(jm, grid, lds, st, a);
+        else launch_a4<4>(jm, grid, lds, st, a);
         return hipGetLastError();
     }
     if (p.norm) {  // one bf16 token, normalized in the prologue (gemv_norm_supported)

@@ -603,3 +603,34 @@ def test_forward_a4(bl, m, k, n):
     r = oracle.forward_a4(x, p_ref, g_ref, k, "bf16")
     np.testing.assert_array_equal(host(acc), r["acc"])
     assert_y_close(host(y), r["y"])
+
+
+# One bf16 token: the 4-bit codes are made in the decode kernel's prologue
+# (the top-K select over its 512 threads). keep = 1, half, all; ragged 64-input
+# blocks; up to four resident groups per thread; and a token whose magnitudes
+# repeat (ties at tau: every entry with |x| >= tau is kept).
+@pytest.mark.parametrize("k,n,keep", [(2576, 300, 1288), (16384, 100, 1), (20000, 64, 20000), (64, 8, 32),
+                                      (6912, 2560, 3456), (2560, 6912, None)])
+def test_forward_a4_decode(bl, k, n, keep):
+    w, p_ref, g_ref, _ = make_linear(183, 1, n, k)
+    x = synth.activations(183, 1, k, dtype="bf16", heavy_channels=max(1, k // 100))
+    packed, gamma = bl.pack_weights(to_dev(w))
+    y, acc = bl.forward_a4(to_dev(x, "bf16"), packed, gamma, keep, return_acc=True)
+    r = oracle.forward_a4(x, p_ref, g_ref, k, "bf16", keep)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"])
+
+
+def test_forward_a4_decode_ties(bl):
+    k, n = 1024, 96
+    w, p_ref, g_ref, _ = make_linear(184, 1, n, k)
+    levels = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -3.0], np.float32)
+    x = levels[np.arange(k) % len(levels)][None, :]
+    xb = synth.f32_to_bf16_bits(x)
+    packed, gamma = bl.pack_weights(to_dev(w))
+    for keep in (1, 100, 300, 512, 1000, k):
+        y, acc = bl.forward_a4(to_dev(xb, "bf16"), packed, gamma, keep, return_acc=True)
+        r = oracle.forward_a4(xb, p_ref, g_ref, k, "bf16", keep)
+        np.testing.assert_array_equal(host(acc), r["acc"])
+        assert_y_close(host(y), r["y"])
+
