@@ -331,7 +331,7 @@ bl_status bitlinear_forward_norm(const void *x, bl_dtype dtype, int64_t m, int64
         if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
         w = L.wpad;
     }
-    if (gemv_norm_supported(m, k, dtype == BL_BF16)) {  // one token: the norm in the decode kernel's prologue
+    if (gemv_token_prologue_supported(m, k, dtype == BL_BF16)) {  // one token: the norm in the decode kernel's prologue
         GemvProblem p{};
         p.x = x; p.bf16 = true; p.m = m; p.k = k; p.kp = L.kp; p.n = n;
         p.w0 = w; p.ldw = L.kp / 4; p.gamma0 = gamma; p.out = y; p.acc_out = acc_out;
@@ -371,7 +371,7 @@ bl_status bitlinear_forward_a4(const void *x, bl_dtype dtype, int64_t m, int64_t
         if (hipError_t e = launch_pad_weights(packed, n, k, L.kp, L.wpad, st)) return hip_status(e);
         w = L.wpad;
     }
-    if (gemv_norm_supported(m, k, dtype == BL_BF16)) {  // one token: the 4-bit codes in the decode kernel's prologue
+    if (gemv_token_prologue_supported(m, k, dtype == BL_BF16)) {  // one token: the 4-bit codes in the decode kernel's prologue
         GemvProblem p{};
         p.x = x; p.bf16 = true; p.m = m; p.k = k; p.kp = L.kp; p.n = n;
         p.w0 = w; p.ldw = L.kp / 4; p.gamma0 = gamma; p.out = y; p.acc_out = acc_out;

@@ -664,7 +664,7 @@ bool gemv_prequant_supported(int64_t m, int64_t kp)
     return gemv_supported(m, kp) && m * (kp / 16) <= (int64_t)kSlots * kGT;
 }
 
-bool gemv_norm_supported(int64_t m, int64_t k, bool bf16)
+bool gemv_token_prologue_supported(int64_t m, int64_t k, bool bf16)
 {
     return m == 1 && bf16 && k % 16 == 0 && gemv_supported(1, round_up(k, 64)) && k / 16 <= (int64_t)kSlots * kGT;
 }
@@ -716,14 +716,14 @@ hipError_t launch_gemv(const GemvProblem &p, hipStream_t st)
         else launch_preq<4>((int)p.m, jm, grid, lds, st, a);
         return hipGetLastError();
     }
-    if (p.a4) {  // one bf16 token, 4-bit codes made in the prologue (gemv_norm_supported)
+    if (p.a4) {  // one bf16 token, 4-bit codes made in the prologue (gemv_token_prologue_supported)
         const int64_t sl = ceil_div(p.k / 16, (int64_t)kGT);
         if (sl <= 1) launch_a4<1>(jm, grid, lds, st, a);
         else if (sl <= 2) launch_a4<2>(jm, grid, lds, st, a);
         else launch_a4<4>(jm, grid, lds, st, a);
         return hipGetLastError();
     }
-    if (p.norm) {  // one bf16 token, normalized in the prologue (gemv_norm_supported)
+    if (p.norm) {  // one bf16 token, normalized in the prologue (gemv_token_prologue_supported)
         const int64_t sl = ceil_div(p.k / 16, (int64_t)kGT);
         if (sl <= 1) launch_norm<1>(jm, grid, lds, st, a);
         else if (sl <= 2) launch_norm<2>(jm, grid, lds, st, a);

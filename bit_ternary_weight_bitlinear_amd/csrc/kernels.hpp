@@ -56,9 +56,9 @@ struct GemvProblem {
     const int32_t *pre_sumq;
     float qmax = 127.0f;     // mode 2: code of the largest magnitude (127 int8, 12 doubled E2M1)
     float *hmax_part;        // gate/up pair, optional: max |h| per (workgroup, token), [grid][m]
-    bool norm = false;       // RMS norm (subln) of the one bf16 token first (gemv_norm_supported)
+    bool norm = false;       // RMS norm (subln) of the one bf16 token first (gemv_token_prologue_supported)
     const float *gain = nullptr;  // norm: per-input gain [k] or NULL
-    bool a4 = false;         // 4-bit top-K E2M1 codes of the one bf16 token (gemv_norm_supported); qmax = 12
+    bool a4 = false;         // 4-bit top-K E2M1 codes of the one bf16 token (gemv_token_prologue_supported); qmax = 12
     int64_t keep = 0;        // a4: entries kept
 };
 bool gemv_supported(int64_t m, int64_t kp);
@@ -66,7 +66,7 @@ bool gemv_supported(int64_t m, int64_t kp);
 bool gemv_prequant_supported(int64_t m, int64_t kp);
 // the decode kernel with the RMS norm or the 4-bit quantization in its
 // prologue: one bf16 token, k % 16 == 0
-bool gemv_norm_supported(int64_t m, int64_t k, bool bf16);
+bool gemv_token_prologue_supported(int64_t m, int64_t k, bool bf16);
 // workgroups of a decode launch (the number of hmax_part rows it writes)
 int64_t gemv_grid(int64_t n, int64_t kp, bool dual);
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
